@@ -1,0 +1,325 @@
+// Reference oracle for the error-compensated 4-bit linear layer.
+//
+// TEST INFRASTRUCTURE ONLY. Nothing in the product path may link, load or
+// call this file; only the tests, the smoke check and the CPU-baseline leg of
+// the benchmark do. It shares no code, header, table or helper with the HIP
+// library: every conversion and every formula below is written out here again,
+// on purpose, in plain double precision, single-threaded, with no blocking,
+// fusion or reordering beyond the definitions it follows.
+//
+// What it computes (sources are the summaries of the SPEAR paper,
+// "SPEAR: A System for Post-Quantization Error-Adaptive Recovery Enabling
+// Efficient Low-Bit LLM Serving", gist.science, in Korean, Japanese and Dutch):
+//
+//   * RTN int4 weight quantization (SPEAR summary, section 3.1, quality
+//     recovery: the hard setting is RTN with per-channel scales). Symmetric
+//     per-output-channel and asymmetric group-wise with zero-points.
+//   * Unpack / dequantization of the packed codes:  W~[n,k] = (c - z) * s.
+//   * The compensated product (SPEAR summary, section 2.1 A, input-adaptive
+//     error compensators): the effective weight for token x is
+//         W~ + alpha * B * diag(gamma(A x)) * A,
+//     with A (r x d_in) projecting x to rank r, gamma a per-token gate on the
+//     projection and B (d_out x r) projecting back. The gate form is the
+//     elementwise sigmoid(g (.) u + b) (the pages call it a lightweight
+//     bottleneck gate without a formula; this is the fixed reading).
+//
+// Readings where the pages are silent (all listed in the design notes):
+//   * RTN rounds half to even (IEEE default).
+//   * symmetric scale = RN_fp16(max|W| / 7), codes c = clamp(rint(W/s),-8,7)+8,
+//     implicit zero-point 8;
+//   * asymmetric range includes 0: lo=min(0,min W), hi=max(0,max W),
+//     s = RN_fp16((hi-lo)/15), z = clamp(rint(-lo/s),0,15),
+//     c = clamp(rint(W/s)+z, 0, 15);
+//   * the scale is rounded to fp16 first and the rounded value is the one used
+//     to quantize; a scale that rounds to 0 becomes 1; fp16 rounding of a scale
+//     saturates at 65504 instead of overflowing;
+//   * ratios are formed in double: s = RN_fp16(fl64(m / 7)).
+//   * packing: code of column k sits in 32-bit word k/8 of its row at bits
+//     4*(k%8); zero-point of group j sits in word j/8 at bits 4*(j%8).
+#include <cmath>
+#include <cstdint>
+#include <cstring>
+#include <vector>
+#include <algorithm>
+
+extern "C" {
+
+// ------------------------------------------------------------------ formats
+
+// IEEE binary16 bits -> double (exact).
+double orc_half_to_double(uint16_t h) {
+  const int sign = h >> 15, e = (h >> 10) & 31, m = h & 1023;
+  double v;
+  if (e == 0) v = std::ldexp((double)m, -24);
+  else if (e == 31) v = m ? NAN : INFINITY;
+  else v = std::ldexp((double)(1024 + m), e - 25);
+  return sign ? -v : v;
+}
+
+// bfloat16 bits -> double (exact): the bits are the top half of a binary32.
+double orc_bf16_to_double(uint16_t b) {
+  uint32_t u = (uint32_t)b << 16;
+  float f;
+  std::memcpy(&f, &u, 4);
+  return (double)f;
+}
+
+// Round a double to the nearest multiple of the binade quantum q = 2^qexp,
+// ties to even. a >= 0. Exact: a/q and n*q only move the exponent.
+static double round_to_quantum(double a, int qexp) {
+  const double q = std::ldexp(1.0, qexp);
+  return std::nearbyint(a / q) * q;
+}
+
+// double -> binary16, round to nearest even, finite overflow saturates at
+// 65504 (reading for scales; never reached by the synthetic workloads).
+uint16_t orc_double_to_half(double v) {
+  if (std::isnan(v)) return 0x7E00;
+  const uint16_t sign = std::signbit(v) ? 0x8000 : 0;
+  double a = std::fabs(v);
+  if (a == 0.0) return sign;
+  int e;
+  std::frexp(a, &e);                 // a = f * 2^e, f in [0.5, 1)
+  const int lead = e - 1;            // weight of the leading bit: 2^lead
+  double r = round_to_quantum(a, std::max(lead, -14) - 10);
+  if (r > 65504.0) r = 65504.0;
+  if (r == 0.0) return sign;
+  if (r < std::ldexp(1.0, -14))      // subnormal: integer multiple of 2^-24
+    return sign | (uint16_t)std::ldexp(r, 24);
+  std::frexp(r, &e);
+  const int l2 = e - 1;
+  const uint16_t mant = (uint16_t)(std::ldexp(r, -l2) * 1024.0 - 1024.0);
+  return sign | (uint16_t)((l2 + 15) << 10) | mant;
+}
+
+// double -> bfloat16, round to nearest even (directly, no detour through
+// binary32, so there is no double rounding); overflow gives infinity.
+uint16_t orc_double_to_bf16(double v) {
+  if (std::isnan(v)) return 0x7FC0;
+  const uint16_t sign = std::signbit(v) ? 0x8000 : 0;
+  double a = std::fabs(v);
+  if (a == 0.0) return sign;
+  int e;
+  std::frexp(a, &e);
+  const int lead = e - 1;
+  double r = round_to_quantum(a, std::max(lead, -126) - 7);
+  if (r >= std::ldexp(1.0, 128)) return sign | 0x7F80;
+  if (r == 0.0) return sign;
+  if (r < std::ldexp(1.0, -126))
+    return sign | (uint16_t)std::ldexp(r, 133);
+  std::frexp(r, &e);
+  const int l2 = e - 1;
+  const uint16_t mant = (uint16_t)(std::ldexp(r, -l2) * 128.0 - 128.0);
+  return sign | (uint16_t)((l2 + 127) << 7) | mant;
+}
+
+// ------------------------------------------------------------ quantization
+
+// One group of g weights (stride 1). Writes codes (0..15) and returns the
+// scale bits and the zero-point.
+static void quantize_group(const float* w, int g, int asym, uint8_t* codes,
+                           uint16_t* scale_bits, int* zero) {
+  if (!asym) {
+    double m = 0.0;
+    for (int k = 0; k < g; ++k) m = std::max(m, std::fabs((double)w[k]));
+    uint16_t sb = orc_double_to_half(m / 7.0);
+    if (orc_half_to_double(sb) == 0.0) sb = 0x3C00;  // 1.0
+    const double s = orc_half_to_double(sb);
+    for (int k = 0; k < g; ++k) {
+      double q = std::nearbyint((double)w[k] / s);
+      q = std::min(7.0, std::max(-8.0, q));
+      codes[k] = (uint8_t)(q + 8.0);
+    }
+    *scale_bits = sb;
+    *zero = 8;
+  } else {
+    double lo = 0.0, hi = 0.0;
+    for (int k = 0; k < g; ++k) {
+      lo = std::min(lo, (double)w[k]);
+      hi = std::max(hi, (double)w[k]);
+    }
+    uint16_t sb = orc_double_to_half((hi - lo) / 15.0);
+    if (orc_half_to_double(sb) == 0.0) sb = 0x3C00;
+    const double s = orc_half_to_double(sb);
+    double z = std::nearbyint(-lo / s);
+    z = std::min(15.0, std::max(0.0, z));
+    for (int k = 0; k < g; ++k) {
+      double c = std::nearbyint((double)w[k] / s) + z;
+      c = std::min(15.0, std::max(0.0, c));
+      codes[k] = (uint8_t)c;
+    }
+    *scale_bits = sb;
+    *zero = (int)z;
+  }
+}
+
+// RTN-quantize W (fp32 [N][K], row-major) with group size g (g == K is
+// per-channel) and pack. wq: uint32 [N][K/8]; scales: fp16 bits [N][K/g];
+// zeros: uint32 [N][ceil((K/g)/8)] (written only when asym != 0).
+// Returns 0, or -1 on a shape it does not accept.
+int orc_quantize_rtn(const float* W, int N, int K, int g, int asym,
+                     uint32_t* wq, uint16_t* scales, uint32_t* zeros) {
+  if (N < 0 || K <= 0 || g <= 0 || K % g != 0 || K % 8 != 0) return -1;
+  const int G = K / g, ZW = (G + 7) / 8;
+  std::vector<uint8_t> codes(g);
+  std::memset(wq, 0, sizeof(uint32_t) * (size_t)N * (K / 8));
+  if (asym) std::memset(zeros, 0, sizeof(uint32_t) * (size_t)N * ZW);
+  for (int n = 0; n < N; ++n) {
+    for (int j = 0; j < G; ++j) {
+      uint16_t sb;
+      int z;
+      quantize_group(W + (size_t)n * K + (size_t)j * g, g, asym, codes.data(), &sb, &z);
+      scales[(size_t)n * G + j] = sb;
+      if (asym) zeros[(size_t)n * ZW + j / 8] |= (uint32_t)z << (4 * (j % 8));
+      for (int kk = 0; kk < g; ++kk) {
+        const int k = j * g + kk;
+        wq[(size_t)n * (K / 8) + k / 8] |= (uint32_t)codes[kk] << (4 * (k % 8));
+      }
+    }
+  }
+  return 0;
+}
+
+// Code of (n, k) and zero-point of (n, j), read back from the packed words.
+int orc_code(const uint32_t* wq, int K, int n, int k) {
+  return (int)((wq[(size_t)n * (K / 8) + k / 8] >> (4 * (k % 8))) & 15u);
+}
+int orc_zero(const uint32_t* zeros, int G, int n, int j) {
+  if (!zeros) return 8;
+  const int ZW = (G + 7) / 8;
+  return (int)((zeros[(size_t)n * ZW + j / 8] >> (4 * (j % 8))) & 15u);
+}
+
+// Dequantized row n: out[k] = (c[n,k] - z[n,k/g]) * s[n,k/g], exact in double.
+static void dequant_row(const uint32_t* wq, const uint16_t* scales, const uint32_t* zeros,
+                        int K, int g, int n, double* out) {
+  const int G = K / g;
+  for (int k = 0; k < K; ++k) {
+    const int j = k / g;
+    const int c = orc_code(wq, K, n, k);
+    const int z = orc_zero(zeros, G, n, j);
+    out[k] = (double)(c - z) * orc_half_to_double(scales[(size_t)n * G + j]);
+  }
+}
+
+// Full dequantized matrix, double [N][K].
+void orc_dequant(const uint32_t* wq, const uint16_t* scales, const uint32_t* zeros,
+                 int N, int K, int g, double* out) {
+  for (int n = 0; n < N; ++n) dequant_row(wq, scales, zeros, K, g, n, out + (size_t)n * K);
+}
+
+// ------------------------------------------------------------- compensator
+
+// Logistic function, written in the form that never overflows exp().
+double orc_sigmoid(double z) {
+  if (z >= 0.0) return 1.0 / (1.0 + std::exp(-z));
+  const double e = std::exp(z);
+  return e / (1.0 + e);
+}
+
+// Rank-r projection of one token and its gate:
+//   u[j] = sum_k A[j,k] x[k];  v[j] = sigmoid(g[j] u[j] + b[j]) * u[j].
+static void project_and_gate(const double* xt, const uint16_t* A, const float* gv,
+                             const float* bv, int r, int K, double* u, double* v) {
+  for (int j = 0; j < r; ++j) {
+    double acc = 0.0;
+    for (int k = 0; k < K; ++k) acc += orc_bf16_to_double(A[(size_t)j * K + k]) * xt[k];
+    u[j] = acc;
+    v[j] = orc_sigmoid((double)gv[j] * acc + (double)bv[j]) * acc;
+  }
+}
+
+// The compensated layer for T tokens:
+//   y[t,n] = sum_k W~[n,k] x[t,k] + alpha * sum_j B[n,j] v[t,j].
+// x: bf16 bits [T][K]; A: bf16 bits [r][K]; B: bf16 bits [N][r];
+// g, b: fp32 [r]; zeros may be NULL (symmetric, z = 8); r may be 0.
+// y: double [T][N]; u, v (optional, may be NULL): double [T][r].
+void orc_forward(int T, int K, int N, int r, int g,
+                 const uint16_t* x, const uint32_t* wq, const uint16_t* scales,
+                 const uint32_t* zeros, const uint16_t* A, const uint16_t* B,
+                 const float* gv, const float* bv, float alpha,
+                 double* y, double* u_out, double* v_out) {
+  std::vector<double> xd((size_t)T * K), w(K), u(r > 0 ? r : 1), v(r > 0 ? r : 1);
+  for (size_t i = 0; i < (size_t)T * K; ++i) xd[i] = orc_bf16_to_double(x[i]);
+  std::vector<double> V((size_t)T * (r > 0 ? r : 1));
+  for (int t = 0; t < T; ++t) {
+    if (r > 0) {
+      project_and_gate(&xd[(size_t)t * K], A, gv, bv, r, K, u.data(), v.data());
+      for (int j = 0; j < r; ++j) {
+        V[(size_t)t * r + j] = v[j];
+        if (u_out) u_out[(size_t)t * r + j] = u[j];
+        if (v_out) v_out[(size_t)t * r + j] = v[j];
+      }
+    }
+  }
+  for (int n = 0; n < N; ++n) {
+    dequant_row(wq, scales, zeros, K, g, n, w.data());
+    for (int t = 0; t < T; ++t) {
+      double acc = 0.0;
+      const double* xt = &xd[(size_t)t * K];
+      for (int k = 0; k < K; ++k) acc += w[k] * xt[k];
+      double corr = 0.0;
+      for (int j = 0; j < r; ++j)
+        corr += orc_bf16_to_double(B[(size_t)n * r + j]) * V[(size_t)t * r + j];
+      y[(size_t)t * N + n] = acc + (double)alpha * corr;
+    }
+  }
+}
+
+// Same quantity at a list of (t, n) positions only (for layers too large to
+// evaluate in full). y[i] = value at (t_idx[i], n_idx[i]).
+void orc_forward_sampled(int T, int K, int N, int r, int g,
+                         const uint16_t* x, const uint32_t* wq, const uint16_t* scales,
+                         const uint32_t* zeros, const uint16_t* A, const uint16_t* B,
+                         const float* gv, const float* bv, float alpha,
+                         int count, const int32_t* t_idx, const int32_t* n_idx, double* y) {
+  (void)N;
+  std::vector<double> xt(K), w(K), u(r > 0 ? r : 1), v(r > 0 ? r : 1);
+  for (int i = 0; i < count; ++i) {
+    const int t = t_idx[i], n = n_idx[i];
+    for (int k = 0; k < K; ++k) xt[k] = orc_bf16_to_double(x[(size_t)t * K + k]);
+    if (r > 0) project_and_gate(xt.data(), A, gv, bv, r, K, u.data(), v.data());
+    dequant_row(wq, scales, zeros, K, g, n, w.data());
+    double acc = 0.0;
+    for (int k = 0; k < K; ++k) acc += w[k] * xt[k];
+    double corr = 0.0;
+    for (int j = 0; j < r; ++j) corr += orc_bf16_to_double(B[(size_t)n * r + j]) * v[j];
+    y[i] = acc + (double)alpha * corr;
+  }
+}
+
+// Brute force through the explicit per-token effective weight
+//   W_eff(t) = W~ + alpha * B diag(gamma(A x_t)) A,   y_t = W_eff(t) x_t,
+// materialising the N x K matrix for every token (tiny shapes only).
+void orc_forward_effective_weight(int T, int K, int N, int r, int g,
+                                  const uint16_t* x, const uint32_t* wq,
+                                  const uint16_t* scales, const uint32_t* zeros,
+                                  const uint16_t* A, const uint16_t* B,
+                                  const float* gv, const float* bv, float alpha,
+                                  double* y) {
+  std::vector<double> Wt((size_t)N * K), Weff((size_t)N * K), xt(K), gam(r > 0 ? r : 1);
+  orc_dequant(wq, scales, zeros, N, K, g, Wt.data());
+  for (int t = 0; t < T; ++t) {
+    for (int k = 0; k < K; ++k) xt[k] = orc_bf16_to_double(x[(size_t)t * K + k]);
+    for (int j = 0; j < r; ++j) {
+      double u = 0.0;
+      for (int k = 0; k < K; ++k) u += orc_bf16_to_double(A[(size_t)j * K + k]) * xt[k];
+      gam[j] = orc_sigmoid((double)gv[j] * u + (double)bv[j]);
+    }
+    for (int n = 0; n < N; ++n)
+      for (int k = 0; k < K; ++k) {
+        double c = 0.0;
+        for (int j = 0; j < r; ++j)
+          c += orc_bf16_to_double(B[(size_t)n * r + j]) * gam[j] *
+               orc_bf16_to_double(A[(size_t)j * K + k]);
+        Weff[(size_t)n * K + k] = Wt[(size_t)n * K + k] + (double)alpha * c;
+      }
+    for (int n = 0; n < N; ++n) {
+      double acc = 0.0;
+      for (int k = 0; k < K; ++k) acc += Weff[(size_t)n * K + k] * xt[k];
+      y[(size_t)t * N + n] = acc;
+    }
+  }
+}
+
+}  // extern "C"
