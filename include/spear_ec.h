@@ -1,0 +1,173 @@
+/*
+ * spear_ec.h -- C ABI of libspear_ec, the error-compensated 4-bit linear layer
+ * for AMD Instinct MI355X (gfx950).
+ *
+ * The layer (SPEAR summary, "SPEAR: A System for Post-Quantization
+ * Error-Adaptive Recovery Enabling Efficient Low-Bit LLM Serving", section
+ * 2.1 A, input-adaptive error compensators) multiplies each token x by the
+ * effective weight
+ *
+ *     W~ + alpha * B * diag(gamma(A x)) * A
+ *
+ * where W~ is the dequantized int4 weight, A (rank x d_in) projects x to a
+ * low rank, gamma is a per-token gate on that projection and B (d_out x rank)
+ * projects back.  The gate is fixed to the elementwise form
+ * gamma(u) = sigmoid(g (.) u + b) with learned vectors g and b (the pages
+ * describe a lightweight gate without giving a formula).  Computed in the
+ * factored form
+ *
+ *     y[t,n] = sum_k W~[n,k] x[t,k] + alpha * sum_j B[n,j] v[t,j],
+ *     u[t,j] = sum_k A[j,k] x[t,k],   v[t,j] = sigmoid(g[j] u[t,j] + b[j]) u[t,j].
+ *
+ * Data formats (all row-major, contiguous, 16-byte aligned device memory):
+ *   x       bf16   [tokens][d_in]
+ *   wq      uint32 [d_out][d_in/8]   code of column k in bits 4*(k%8) of word k/8
+ *   scales  fp16   [d_out][d_in/group_size]
+ *   zeros   uint32 [d_out][ceil(G/8)] zero-point of group j in bits 4*(j%8) of
+ *           word j/8; NULL means symmetric codes with implicit zero-point 8
+ *   A       bf16   [rank][d_in]
+ *   B       bf16   [d_out][rank]
+ *   g, b    fp32   [rank]
+ *   y       bf16   [tokens][d_out], written once per call (round to nearest even)
+ * Dequantization: W~[n,k] = (c[n,k] - z[n,k/g]) * s[n,k/g], exact in fp32.
+ *
+ * Conventions shared by every entry point:
+ *   - All pointers are caller-owned device pointers; the library keeps none
+ *     of them after the call returns and allocates nothing.
+ *   - Calls are asynchronous on `stream` (NULL = the default stream); there is
+ *     no host synchronisation inside a call.
+ *   - Every argument is validated before any HIP call; on a validation error
+ *     nothing is launched and the status code says why.  No C++ exception
+ *     crosses this interface.  spear_ec_last_error() gives a thread-local text
+ *     for the last failure.
+ *   - `y` must not alias any input.
+ */
+#ifndef SPEAR_EC_H
+#define SPEAR_EC_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define SPEAR_EC_VERSION 1
+
+/* Status codes. */
+#define SPEAR_EC_OK 0
+#define SPEAR_EC_ERR_INVALID_ARGUMENT 1 /* NULL required pointer, negative size, bad desc */
+#define SPEAR_EC_ERR_UNSUPPORTED 2      /* shape or format outside the supported set      */
+#define SPEAR_EC_ERR_MISALIGNED 3       /* a pointer is not 16-byte aligned                */
+#define SPEAR_EC_ERR_WORKSPACE 4        /* workspace NULL or smaller than required         */
+#define SPEAR_EC_ERR_HIP 5              /* HIP launch / runtime error (see last_error)     */
+
+/* desc.flags */
+#define SPEAR_EC_ZEROS 1 /* asymmetric codes: `zeros` is present and required */
+
+/* Largest token count the decode path accepts (decode = 1..32 tokens). */
+#define SPEAR_EC_DECODE_MAX_TOKENS 32
+
+/*
+ * Shapes and weight format of one layer.  Supported set:
+ *   d_in       multiple of 128, 128 .. 131072
+ *   d_out      multiple of 16, 16 .. 131072
+ *   rank       0 (plain W4, no compensator) or a multiple of 16 up to 128
+ *   group_size d_in (per-output-channel scales) or 128
+ *   flags      0 or SPEAR_EC_ZEROS
+ * Passed by pointer and read during the call only.
+ */
+typedef struct spear_ec_desc {
+  int32_t d_in;
+  int32_t d_out;
+  int32_t rank;
+  int32_t group_size;
+  int32_t flags;
+} spear_ec_desc;
+
+/*
+ * Bytes of scratch device memory one call with up to `max_tokens` tokens
+ * needs (either path).  The workspace holds the rank-r projections, per-block
+ * sums of x, split-K partial sums and a few arrival counters.  Its first use
+ * requires it to be zero-filled by the caller (hipMemset once after
+ * allocation); every call leaves the counters at zero again.  One workspace
+ * per stream: calls that overlap on one workspace race.  Returns 0 for an
+ * invalid desc or max_tokens < 0.
+ */
+size_t spear_ec_workspace_bytes(const spear_ec_desc* desc, int32_t max_tokens);
+
+/*
+ * Phase-aware dispatch (SPEAR summary, section 2.2 A, phase-aware adaptive
+ * kernel fusion dispatch: memory-bound decode fuses the compensator into the
+ * low-bit GEMM epilogue; compute-bound prefill takes the GEMM path).
+ * tokens <= SPEAR_EC_DECODE_MAX_TOKENS runs spear_ec_linear_decode, larger
+ * batches run spear_ec_linear_prefill.  tokens == 0 returns SPEAR_EC_OK and
+ * launches nothing.  With rank == 0, A, B, g and b may be NULL and alpha is
+ * ignored.
+ */
+int spear_ec_linear(const spear_ec_desc* desc, int32_t tokens, const void* x,
+                    const uint32_t* wq, const void* scales, const uint32_t* zeros,
+                    const void* A, const void* B, const float* g, const float* b,
+                    float alpha, void* y, void* workspace, size_t workspace_bytes,
+                    hipStream_t stream);
+
+/*
+ * Decode path, 1..32 tokens (memory-bound: streams the packed weights once;
+ * the rank-r projection is computed once per token and the gated B term is
+ * added in registers before the single store of y).  tokens > 32 returns
+ * SPEAR_EC_ERR_UNSUPPORTED.  Same arguments as spear_ec_linear.
+ */
+int spear_ec_linear_decode(const spear_ec_desc* desc, int32_t tokens, const void* x,
+                           const uint32_t* wq, const void* scales, const uint32_t* zeros,
+                           const void* A, const void* B, const float* g, const float* b,
+                           float alpha, void* y, void* workspace, size_t workspace_bytes,
+                           hipStream_t stream);
+
+/*
+ * Prefill path, any token count >= 1 (compute-bound: matrix-core GEMM on
+ * exact integer codes with the scales applied in fp32; the gated B term is a
+ * small matrix-core product added to the same accumulators before the
+ * store).  Same arguments as spear_ec_linear.
+ */
+int spear_ec_linear_prefill(const spear_ec_desc* desc, int32_t tokens, const void* x,
+                            const uint32_t* wq, const void* scales, const uint32_t* zeros,
+                            const void* A, const void* B, const float* g, const float* b,
+                            float alpha, void* y, void* workspace, size_t workspace_bytes,
+                            hipStream_t stream);
+
+/*
+ * Round-to-nearest int4 quantization of fp32 weights w [d_out][d_in] into the
+ * packed format above (offline preparation; SPEAR summary, section 3.1: RTN
+ * with per-channel scales is the hardest setting the compensators target).
+ * Without SPEAR_EC_ZEROS: symmetric, s = RN_fp16(max|W|/7), codes
+ * clamp(rint(W/s), -8, 7) + 8.  With SPEAR_EC_ZEROS: asymmetric over the range
+ * widened to include 0, s = RN_fp16((hi - lo)/15), z = clamp(rint(-lo/s), 0, 15),
+ * codes clamp(rint(W/s) + z, 0, 15).  Ratios are formed in double, rint rounds
+ * half to even, a scale that rounds to 0 becomes 1, and fp16 rounding of a
+ * scale saturates at 65504.  `zeros` is written only with SPEAR_EC_ZEROS.
+ * desc.rank is ignored.
+ */
+int spear_ec_quantize_rtn(const spear_ec_desc* desc, const float* w, uint32_t* wq,
+                          void* scales, uint32_t* zeros, hipStream_t stream);
+
+/*
+ * Dequantize the packed weights to fp32 w_out [d_out][d_in]:
+ * (c - z) * s, exact.  Used to check the unpack path bit for bit.
+ */
+int spear_ec_dequant_f32(const spear_ec_desc* desc, const uint32_t* wq, const void* scales,
+                         const uint32_t* zeros, float* w_out, hipStream_t stream);
+
+/* Static text for a status code. */
+const char* spear_ec_status_string(int status);
+
+/* Thread-local text describing the last failure on this thread ("" if none). */
+const char* spear_ec_last_error(void);
+
+/* SPEAR_EC_VERSION of the built library. */
+int spear_ec_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* SPEAR_EC_H */

@@ -1,0 +1,156 @@
+"""Python binding of libspear_ec (ctypes; argument marshalling only).
+
+Every function here has the name of the C entry point it calls and does
+nothing but turn torch tensors into device pointers, pick the current HIP
+stream, and raise on a non-zero status.  All computation happens in the HIP
+kernels of libspear_ec.so.  There is no fallback: if the library is missing,
+importing the functions raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libspear_ec.so")
+HEADER = os.path.join(os.path.dirname(HERE), "include", "spear_ec.h")
+
+SPEAR_EC_OK = 0
+SPEAR_EC_ERR_INVALID_ARGUMENT = 1
+SPEAR_EC_ERR_UNSUPPORTED = 2
+SPEAR_EC_ERR_MISALIGNED = 3
+SPEAR_EC_ERR_WORKSPACE = 4
+SPEAR_EC_ERR_HIP = 5
+SPEAR_EC_ZEROS = 1
+SPEAR_EC_DECODE_MAX_TOKENS = 32
+
+EXPORTED = (
+    "spear_ec_workspace_bytes", "spear_ec_linear", "spear_ec_linear_decode",
+    "spear_ec_linear_prefill", "spear_ec_quantize_rtn", "spear_ec_dequant_f32",
+    "spear_ec_status_string", "spear_ec_last_error", "spear_ec_version",
+)
+
+
+class spear_ec_desc(ctypes.Structure):
+    _fields_ = [("d_in", ctypes.c_int32), ("d_out", ctypes.c_int32), ("rank", ctypes.c_int32),
+                ("group_size", ctypes.c_int32), ("flags", ctypes.c_int32)]
+
+
+class SpearEcError(RuntimeError):
+    def __init__(self, status: int, text: str):
+        super().__init__(f"libspear_ec status {status}: {text}")
+        self.status = status
+
+
+_lib = None
+
+
+def load_library(path: str = LIB_PATH):
+    """Load libspear_ec.so (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is missing: build it with "
+                           "`python -m quantization_error_compensation_amd.build`")
+    lib = ctypes.CDLL(path)
+    P, i32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t
+    DP = ctypes.POINTER(spear_ec_desc)
+    lib.spear_ec_workspace_bytes.argtypes = [DP, i32]
+    lib.spear_ec_workspace_bytes.restype = sz
+    lin = [DP, i32, P, P, P, P, P, P, P, P, ctypes.c_float, P, P, sz, P]
+    for name in ("spear_ec_linear", "spear_ec_linear_decode", "spear_ec_linear_prefill"):
+        getattr(lib, name).argtypes = lin
+        getattr(lib, name).restype = ctypes.c_int
+    lib.spear_ec_quantize_rtn.argtypes = [DP, P, P, P, P, P]
+    lib.spear_ec_quantize_rtn.restype = ctypes.c_int
+    lib.spear_ec_dequant_f32.argtypes = [DP, P, P, P, P, P]
+    lib.spear_ec_dequant_f32.restype = ctypes.c_int
+    lib.spear_ec_status_string.argtypes = [ctypes.c_int]
+    lib.spear_ec_status_string.restype = ctypes.c_char_p
+    lib.spear_ec_last_error.argtypes = []
+    lib.spear_ec_last_error.restype = ctypes.c_char_p
+    lib.spear_ec_version.argtypes = []
+    lib.spear_ec_version.restype = ctypes.c_int
+    _lib = lib
+    return lib
+
+
+def make_desc(d_in: int, d_out: int, rank: int, group_size: int, zeros: bool) -> spear_ec_desc:
+    return spear_ec_desc(d_in, d_out, rank, group_size, SPEAR_EC_ZEROS if zeros else 0)
+
+
+def _ptr(t):
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    if stream is None:
+        import torch
+        return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    if isinstance(stream, int):
+        return ctypes.c_void_p(stream)
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _check(status: int):
+    if status != SPEAR_EC_OK:
+        lib = load_library()
+        raise SpearEcError(status, (lib.spear_ec_last_error() or b"").decode() or
+                           lib.spear_ec_status_string(status).decode())
+
+
+def spear_ec_version() -> int:
+    return load_library().spear_ec_version()
+
+
+def spear_ec_status_string(status: int) -> str:
+    return load_library().spear_ec_status_string(status).decode()
+
+
+def spear_ec_last_error() -> str:
+    return load_library().spear_ec_last_error().decode()
+
+
+def spear_ec_workspace_bytes(desc: spear_ec_desc, max_tokens: int) -> int:
+    return int(load_library().spear_ec_workspace_bytes(ctypes.byref(desc), int(max_tokens)))
+
+
+def _linear(name, desc, x, wq, scales, zeros, A, B, g, b, alpha, y, workspace, stream):
+    tokens = int(x.shape[0])
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    fn = getattr(load_library(), name)
+    _check(fn(ctypes.byref(desc), tokens, _ptr(x), _ptr(wq), _ptr(scales), _ptr(zeros), _ptr(A),
+              _ptr(B), _ptr(g), _ptr(b), float(alpha), _ptr(y), _ptr(workspace), ws_bytes,
+              _stream(stream)))
+
+
+def spear_ec_linear(desc, x, wq, scales, zeros, A, B, g, b, alpha, y, workspace, stream=None):
+    """Phase-aware dispatch: decode for <= 32 tokens, prefill above."""
+    _linear("spear_ec_linear", desc, x, wq, scales, zeros, A, B, g, b, alpha, y, workspace, stream)
+
+
+def spear_ec_linear_decode(desc, x, wq, scales, zeros, A, B, g, b, alpha, y, workspace,
+                           stream=None):
+    _linear("spear_ec_linear_decode", desc, x, wq, scales, zeros, A, B, g, b, alpha, y,
+            workspace, stream)
+
+
+def spear_ec_linear_prefill(desc, x, wq, scales, zeros, A, B, g, b, alpha, y, workspace,
+                            stream=None):
+    _linear("spear_ec_linear_prefill", desc, x, wq, scales, zeros, A, B, g, b, alpha, y,
+            workspace, stream)
+
+
+def spear_ec_quantize_rtn(desc, w, wq, scales, zeros, stream=None):
+    _check(load_library().spear_ec_quantize_rtn(ctypes.byref(desc), _ptr(w), _ptr(wq),
+                                                _ptr(scales), _ptr(zeros), _stream(stream)))
+
+
+def spear_ec_dequant_f32(desc, wq, scales, zeros, w_out, stream=None):
+    _check(load_library().spear_ec_dequant_f32(ctypes.byref(desc), _ptr(wq), _ptr(scales),
+                                               _ptr(zeros), _ptr(w_out), _stream(stream)))

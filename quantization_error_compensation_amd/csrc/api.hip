@@ -1,0 +1,255 @@
+// C ABI of libspear_ec: argument validation, work planning, workspace
+// layout and the phase-aware dispatcher.  Every check runs before any HIP
+// call; no C++ exception leaves this file.
+#include <stdio.h>
+#include <string.h>
+
+#include <algorithm>
+
+#include "../../include/spear_ec.h"
+#include "internal.hpp"
+
+namespace spear {
+
+static thread_local char g_last_error[256] = "";
+
+static int fail(int code, const char* msg) {
+  snprintf(g_last_error, sizeof(g_last_error), "%s", msg);
+  return code;
+}
+
+ProjPlan plan_projection(const Shape& s) {
+  ProjPlan pl;
+  pl.tiles = (s.T + kProjTokens - 1) / kProjTokens;
+  const int KB = s.KB();
+  const int want = (512 + pl.tiles - 1) / std::max(pl.tiles, 1);
+  pl.splits = std::max(1, std::min(want, KB / 4));
+  return pl;
+}
+
+DecodePlan plan_decode(const Shape& s) {
+  DecodePlan pl;
+  pl.bands = (s.N + kDecodeBandRows - 1) / kDecodeBandRows;
+  const int KB = s.KB();
+  const int want = (512 + pl.bands - 1) / pl.bands;
+  pl.splits = std::max(1, std::min(want, KB / 4));
+  return pl;
+}
+
+static size_t up256(size_t v) { return (v + 255) & ~(size_t)255; }
+
+Workspace layout(const Shape& s, bool decode) {
+  const ProjPlan pp = plan_projection(s);
+  const size_t T = (size_t)s.T, r = (size_t)s.r, Tp = (size_t)pp.tiles * kProjTokens;
+  Workspace w;
+  size_t o = 0;
+  w.counters = o; o = up256(o + sizeof(int) * kCounterSlots);
+  w.wv32 = o;     o = up256(o + sizeof(float) * T * r);
+  w.wvhi = o;     o = up256(o + 2 * T * r);
+  w.wvlo = o;     o = up256(o + 2 * T * r);
+  w.sblk = o;     o = up256(o + sizeof(float) * (size_t)s.KB() * Tp);
+  w.stot = o;     o = up256(o + sizeof(float) * Tp);
+  w.upart = o;    o = up256(o + sizeof(float) * (size_t)pp.splits * T * (r + 1));
+  w.ypart = o;
+  if (decode) {
+    const DecodePlan dp = plan_decode(s);
+    o = up256(o + sizeof(float) * (size_t)dp.splits * T * (size_t)s.N);
+  }
+  w.total = o;
+  return w;
+}
+
+WsPtrs carve(void* base, const Workspace& w) {
+  char* b = static_cast<char*>(base);
+  WsPtrs p;
+  p.counters = reinterpret_cast<int*>(b + w.counters);
+  p.wv32 = reinterpret_cast<float*>(b + w.wv32);
+  p.wvhi = reinterpret_cast<uint16_t*>(b + w.wvhi);
+  p.wvlo = reinterpret_cast<uint16_t*>(b + w.wvlo);
+  p.sblk = reinterpret_cast<float*>(b + w.sblk);
+  p.stot = reinterpret_cast<float*>(b + w.stot);
+  p.upart = reinterpret_cast<float*>(b + w.upart);
+  p.ypart = reinterpret_cast<float*>(b + w.ypart);
+  return p;
+}
+
+static bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+// Shape checks shared by every entry point.
+static int check_desc(const spear_ec_desc* d, bool need_rank) {
+  if (!d) return fail(SPEAR_EC_ERR_INVALID_ARGUMENT, "desc is NULL");
+  if (d->d_in <= 0 || d->d_out <= 0 || d->rank < 0 || d->group_size <= 0)
+    return fail(SPEAR_EC_ERR_INVALID_ARGUMENT, "desc has a non-positive size");
+  if (d->flags & ~SPEAR_EC_ZEROS) return fail(SPEAR_EC_ERR_INVALID_ARGUMENT, "unknown desc.flags bits");
+  if (d->d_in % 128 != 0 || d->d_in > 131072)
+    return fail(SPEAR_EC_ERR_UNSUPPORTED, "d_in must be a multiple of 128 and at most 131072");
+  if (d->d_out % 16 != 0 || d->d_out > 131072)
+    return fail(SPEAR_EC_ERR_UNSUPPORTED, "d_out must be a multiple of 16 and at most 131072");
+  if (d->group_size != d->d_in && d->group_size != 128)
+    return fail(SPEAR_EC_ERR_UNSUPPORTED, "group_size must be d_in (per-channel) or 128");
+  if (need_rank && (d->rank % 16 != 0 || d->rank > 128))
+    return fail(SPEAR_EC_ERR_UNSUPPORTED, "rank must be 0 or a multiple of 16 up to 128");
+  return SPEAR_EC_OK;
+}
+
+static Shape make_shape(const spear_ec_desc* d, int T) {
+  Shape s;
+  s.K = d->d_in;
+  s.N = d->d_out;
+  s.r = d->rank;
+  s.g = d->group_size;
+  s.T = T;
+  s.grouped = d->group_size == 128 && d->d_in != 128;
+  s.zeros = (d->flags & SPEAR_EC_ZEROS) != 0;
+  return s;
+}
+
+static int hip_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return SPEAR_EC_OK;
+  snprintf(g_last_error, sizeof(g_last_error), "%s: %s", what, hipGetErrorString(e));
+  return SPEAR_EC_ERR_HIP;
+}
+
+enum Path { kAuto, kDecode, kPrefill };
+
+static int linear(Path path, const spear_ec_desc* d, int32_t tokens, const void* x,
+                  const uint32_t* wq, const void* scales, const uint32_t* zeros, const void* A,
+                  const void* B, const float* g, const float* b, float alpha, void* y,
+                  void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  g_last_error[0] = 0;
+  int rc = check_desc(d, true);
+  if (rc) return rc;
+  if (tokens < 0) return fail(SPEAR_EC_ERR_INVALID_ARGUMENT, "tokens is negative");
+  if (tokens > 65536) return fail(SPEAR_EC_ERR_UNSUPPORTED, "tokens must be at most 65536");
+  if (path == kDecode && tokens > SPEAR_EC_DECODE_MAX_TOKENS)
+    return fail(SPEAR_EC_ERR_UNSUPPORTED, "decode path takes at most 32 tokens");
+  if (tokens == 0) return SPEAR_EC_OK;
+  const bool has_z = (d->flags & SPEAR_EC_ZEROS) != 0;
+  if (!x || !wq || !scales || !y) return fail(SPEAR_EC_ERR_INVALID_ARGUMENT, "x, wq, scales and y are required");
+  if (has_z && !zeros) return fail(SPEAR_EC_ERR_INVALID_ARGUMENT, "zeros is required with SPEAR_EC_ZEROS");
+  if (d->rank > 0 && (!A || !B || !g || !b))
+    return fail(SPEAR_EC_ERR_INVALID_ARGUMENT, "A, B, g and b are required when rank > 0");
+  if (!workspace) return fail(SPEAR_EC_ERR_WORKSPACE, "workspace is NULL");
+  const void* ptrs[] = {x, wq, scales, y, workspace, has_z ? zeros : nullptr,
+                        d->rank ? A : nullptr, d->rank ? B : nullptr, d->rank ? g : nullptr,
+                        d->rank ? b : nullptr};
+  for (const void* p : ptrs)
+    if (p && !aligned16(p)) return fail(SPEAR_EC_ERR_MISALIGNED, "a pointer is not 16-byte aligned");
+  const bool decode = path == kDecode || (path == kAuto && tokens <= SPEAR_EC_DECODE_MAX_TOKENS);
+  const Shape s = make_shape(d, tokens);
+  const Workspace wl = layout(s, decode);
+  if (workspace_bytes < wl.total) return fail(SPEAR_EC_ERR_WORKSPACE, "workspace is smaller than spear_ec_workspace_bytes()");
+
+  LayerArgs a;
+  a.x = x;
+  a.wq = wq;
+  a.scales = static_cast<const uint16_t*>(scales);
+  a.zeros = has_z ? zeros : nullptr;
+  a.A = d->rank ? A : nullptr;
+  a.B = d->rank ? B : nullptr;
+  a.gv = d->rank ? g : nullptr;
+  a.bv = d->rank ? b : nullptr;
+  a.alpha = alpha;
+  a.y = y;
+  const WsPtrs wp = carve(workspace, wl);
+  rc = hip_status(launch_projection(s, a, wp, stream), "projection kernel launch");
+  if (rc) return rc;
+  if (decode) return hip_status(launch_decode(s, a, wp, stream), "decode kernel launch");
+  return hip_status(launch_prefill(s, a, wp, stream), "prefill kernel launch");
+}
+
+}  // namespace spear
+
+using namespace spear;
+
+extern "C" {
+
+size_t spear_ec_workspace_bytes(const spear_ec_desc* desc, int32_t max_tokens) {
+  if (check_desc(desc, true) != SPEAR_EC_OK || max_tokens < 0 || max_tokens > 65536) return 0;
+  size_t need = 0;
+  const int td = std::min<int32_t>(max_tokens, SPEAR_EC_DECODE_MAX_TOKENS);
+  // Region sizes grow with the token count, so the largest count of each path bounds it.
+  for (int t : {td, (int)max_tokens}) {
+    if (t <= 0) continue;
+    const Shape s = make_shape(desc, t);
+    need = std::max(need, layout(s, false).total);
+    if (t <= SPEAR_EC_DECODE_MAX_TOKENS) need = std::max(need, layout(s, true).total);
+  }
+  if (need == 0) need = layout(make_shape(desc, 1), false).total;
+  return need;
+}
+
+int spear_ec_linear(const spear_ec_desc* desc, int32_t tokens, const void* x, const uint32_t* wq,
+                    const void* scales, const uint32_t* zeros, const void* A, const void* B,
+                    const float* g, const float* b, float alpha, void* y, void* workspace,
+                    size_t workspace_bytes, hipStream_t stream) {
+  return linear(kAuto, desc, tokens, x, wq, scales, zeros, A, B, g, b, alpha, y, workspace,
+                workspace_bytes, stream);
+}
+
+int spear_ec_linear_decode(const spear_ec_desc* desc, int32_t tokens, const void* x,
+                           const uint32_t* wq, const void* scales, const uint32_t* zeros,
+                           const void* A, const void* B, const float* g, const float* b,
+                           float alpha, void* y, void* workspace, size_t workspace_bytes,
+                           hipStream_t stream) {
+  return linear(kDecode, desc, tokens, x, wq, scales, zeros, A, B, g, b, alpha, y, workspace,
+                workspace_bytes, stream);
+}
+
+int spear_ec_linear_prefill(const spear_ec_desc* desc, int32_t tokens, const void* x,
+                            const uint32_t* wq, const void* scales, const uint32_t* zeros,
+                            const void* A, const void* B, const float* g, const float* b,
+                            float alpha, void* y, void* workspace, size_t workspace_bytes,
+                            hipStream_t stream) {
+  return linear(kPrefill, desc, tokens, x, wq, scales, zeros, A, B, g, b, alpha, y, workspace,
+                workspace_bytes, stream);
+}
+
+int spear_ec_quantize_rtn(const spear_ec_desc* desc, const float* w, uint32_t* wq, void* scales,
+                          uint32_t* zeros, hipStream_t stream) {
+  g_last_error[0] = 0;
+  int rc = check_desc(desc, false);
+  if (rc) return rc;
+  const bool asym = (desc->flags & SPEAR_EC_ZEROS) != 0;
+  if (!w || !wq || !scales || (asym && !zeros))
+    return fail(SPEAR_EC_ERR_INVALID_ARGUMENT, "w, wq, scales (and zeros when asymmetric) are required");
+  if (!aligned16(w) || !aligned16(wq) || !aligned16(scales) || (asym && !aligned16(zeros)))
+    return fail(SPEAR_EC_ERR_MISALIGNED, "a pointer is not 16-byte aligned");
+  return hip_status(launch_quantize(desc->d_out, desc->d_in, desc->group_size, asym, w, wq,
+                                    static_cast<uint16_t*>(scales), asym ? zeros : nullptr, stream),
+                    "quantize kernel launch");
+}
+
+int spear_ec_dequant_f32(const spear_ec_desc* desc, const uint32_t* wq, const void* scales,
+                         const uint32_t* zeros, float* w_out, hipStream_t stream) {
+  g_last_error[0] = 0;
+  int rc = check_desc(desc, false);
+  if (rc) return rc;
+  const bool asym = (desc->flags & SPEAR_EC_ZEROS) != 0;
+  if (!wq || !scales || !w_out || (asym && !zeros))
+    return fail(SPEAR_EC_ERR_INVALID_ARGUMENT, "wq, scales, w_out (and zeros when asymmetric) are required");
+  if (!aligned16(wq) || !aligned16(scales) || !aligned16(w_out) || (asym && !aligned16(zeros)))
+    return fail(SPEAR_EC_ERR_MISALIGNED, "a pointer is not 16-byte aligned");
+  return hip_status(launch_dequant(desc->d_out, desc->d_in, desc->group_size, wq,
+                                   static_cast<const uint16_t*>(scales), asym ? zeros : nullptr,
+                                   w_out, stream),
+                    "dequant kernel launch");
+}
+
+const char* spear_ec_status_string(int status) {
+  switch (status) {
+    case SPEAR_EC_OK: return "ok";
+    case SPEAR_EC_ERR_INVALID_ARGUMENT: return "invalid argument";
+    case SPEAR_EC_ERR_UNSUPPORTED: return "unsupported shape or format";
+    case SPEAR_EC_ERR_MISALIGNED: return "misaligned pointer";
+    case SPEAR_EC_ERR_WORKSPACE: return "workspace missing or too small";
+    case SPEAR_EC_ERR_HIP: return "HIP error";
+    default: return "unknown status";
+  }
+}
+
+const char* spear_ec_last_error(void) { return g_last_error; }
+
+int spear_ec_version(void) { return SPEAR_EC_VERSION; }
+
+}  // extern "C"

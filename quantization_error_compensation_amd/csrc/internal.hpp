@@ -1,0 +1,83 @@
+// Host-side plan of one call: work decomposition and workspace layout, shared
+// by the entry points (api.hip) and the kernel launchers.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace spear {
+
+constexpr int kBlockK = 128;          // K block: one scale group (g = 128) or a slice of a row
+constexpr int kDecodeBandRows = 64;   // output rows per decode workgroup
+constexpr int kProjTokens = 32;       // tokens per projection workgroup
+constexpr int kPrefillBM = 128;       // tokens per prefill tile
+constexpr int kPrefillBN = 128;       // output rows per prefill tile
+constexpr int kCounterSlots = 16384;  // int32 arrival counters at the head of the workspace
+constexpr int kProjCounterBase = 0;   // [0, 8192): projection, one per token tile
+constexpr int kDecodeCounterBase = 8192;  // [8192, 16384): decode, one per row band
+
+struct Shape {
+  int K, N, r, g, T;
+  bool grouped;  // g == 128 (per-group scales); otherwise g == K
+  bool zeros;
+  int KB() const { return K / kBlockK; }
+};
+
+// Work split of the rank-r projection for T tokens.
+struct ProjPlan {
+  int tiles;   // token tiles of kProjTokens
+  int splits;  // K splits
+};
+
+// Work split of the decode GEMV.
+struct DecodePlan {
+  int bands;   // N / 64 (rounded up)
+  int splits;  // K splits across workgroups
+};
+
+ProjPlan plan_projection(const Shape& s);
+DecodePlan plan_decode(const Shape& s);
+
+// Byte offsets of the workspace regions for one call.
+struct Workspace {
+  size_t counters, wv32, wvhi, wvlo, sblk, stot, upart, ypart, total;
+};
+Workspace layout(const Shape& s, bool decode);
+
+// Pointers into a caller workspace.
+struct WsPtrs {
+  int* counters;
+  float* wv32;     // [T][r]      alpha * gated projection
+  uint16_t* wvhi;  // [T][r]      bf16 high part of alpha * v
+  uint16_t* wvlo;  // [T][r]      bf16 remainder
+  float* sblk;     // [KB][T]     sum of x over each 128-column block
+  float* stot;     // [T]         sum of x over the whole row
+  float* upart;    // [splits][T][r + 1] projection partials (+ row-sum partial)
+  float* ypart;    // [splits][T][N] decode partials
+};
+WsPtrs carve(void* base, const Workspace& w);
+
+struct LayerArgs {
+  const void* x;
+  const uint32_t* wq;
+  const uint16_t* scales;
+  const uint32_t* zeros;
+  const void* A;
+  const void* B;
+  const float* gv;
+  const float* bv;
+  float alpha;
+  void* y;
+};
+
+hipError_t launch_projection(const Shape& s, const LayerArgs& a, const WsPtrs& w,
+                             hipStream_t st);
+hipError_t launch_decode(const Shape& s, const LayerArgs& a, const WsPtrs& w, hipStream_t st);
+hipError_t launch_prefill(const Shape& s, const LayerArgs& a, const WsPtrs& w, hipStream_t st);
+hipError_t launch_quantize(int N, int K, int g, bool asym, const float* w, uint32_t* wq,
+                           uint16_t* scales, uint32_t* zeros, hipStream_t st);
+hipError_t launch_dequant(int N, int K, int g, const uint32_t* wq, const uint16_t* scales,
+                          const uint32_t* zeros, float* out, hipStream_t st);
+
+}  // namespace spear

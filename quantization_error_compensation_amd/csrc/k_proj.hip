@@ -1,0 +1,189 @@
+// Rank-r projection and gate of the error compensator, once per token.
+//
+// SPEAR summary, section 2.1 A (input-adaptive error compensators): the
+// compensator projects the activation x into a low-rank space with A and
+// gates each token's projection.  This kernel computes, for every token,
+//     u[t,j] = sum_k A[j,k] x[t,k]                 (matrix cores, fp32 acc)
+//     wv[t,j] = alpha * sigmoid(g[j] u[t,j] + b[j]) * u[t,j]
+// plus the per-128-column sums of x that the main kernels use to remove the
+// +128 offset of their integer-code operands, and the whole-row sums.
+//
+// Work split: one workgroup per (32-token tile, K split).  The four waves of a
+// workgroup take contiguous runs of 128-column blocks; partial u of the split
+// goes to the workspace and the last workgroup to arrive for a token tile sums
+// the partials in split order (deterministic), applies the gate and publishes.
+#include "common.hpp"
+#include "internal.hpp"
+
+namespace spear {
+namespace {
+
+struct ProjParams {
+  const uint16_t* x;   // [T][K] bf16
+  const uint16_t* A;   // [r][K] bf16
+  const float* gv;     // [r]
+  const float* bv;     // [r]
+  float alpha;
+  float* upart;        // [splits][T][r + 1]
+  float* sblk;         // [KB][Tp]
+  float* stot;         // [T]
+  float* wv32;         // [T][r]
+  uint16_t* wvhi;      // [T][r]
+  uint16_t* wvlo;      // [T][r]
+  int* counters;       // one per token tile
+  int T, K, r, Tp, splits;
+};
+
+template <int RTX>  // RTX = r / 16 rank tiles
+__global__ __launch_bounds__(256, 2) void projection_kernel(ProjParams p) {
+  constexpr int MT = 2;  // 32 tokens per workgroup = two 16-row MFMA tiles
+  constexpr int RA = RTX > 0 ? RTX : 1;  // array extent (rank 0 still sums x)
+  __shared__ float red[4][MT][RTX + 1][4][64];
+  __shared__ int s_last;
+
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int q = lane >> 4, c16 = lane & 15;
+  const int tile = blockIdx.x, split = blockIdx.y;
+  const int KB = p.K / kBlockK;
+  const int kb0 = (int)((long long)KB * split / p.splits);
+  const int kb1 = (int)((long long)KB * (split + 1) / p.splits);
+  const int nb = kb1 - kb0;
+  const int wb0 = kb0 + nb * wave / 4, wb1 = kb0 + nb * (wave + 1) / 4;
+  const int t0 = tile * kProjTokens;
+
+  const uint16_t* xr[MT];
+  bool tok_ok[MT];
+  for (int mt = 0; mt < MT; ++mt) {
+    const int t = t0 + 16 * mt + c16;
+    tok_ok[mt] = t < p.T;
+    xr[mt] = p.x + (size_t)(tok_ok[mt] ? t : 0) * p.K + 32 * q;
+  }
+  const uint16_t* ar[RA];
+  for (int rt = 0; rt < RTX; ++rt) ar[rt] = p.A + (size_t)(16 * rt + c16) * p.K + 32 * q;
+
+  f32x4 u[MT][RA];
+  f32x4 ssum[MT];
+  for (int mt = 0; mt < MT; ++mt) {
+    ssum[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int rt = 0; rt < RTX; ++rt) u[mt][rt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+  const u32x4 ones = {kBf16One, kBf16One, kBf16One, kBf16One};
+
+  for (int blk = wb0; blk < wb1; ++blk) {
+    u32x4 xf[MT][4], af[RA][4];
+    for (int mt = 0; mt < MT; ++mt)
+      for (int i = 0; i < 4; ++i)
+        xf[mt][i] = tok_ok[mt] ? load16(xr[mt] + (size_t)blk * kBlockK + 8 * i) : u32x4{0, 0, 0, 0};
+    for (int rt = 0; rt < RTX; ++rt)
+      for (int i = 0; i < 4; ++i) af[rt][i] = load16(ar[rt] + (size_t)blk * kBlockK + 8 * i);
+    for (int mt = 0; mt < MT; ++mt) {
+      f32x4 sb = mfma16x16x32(xf[mt][0], ones, f32x4{0.f, 0.f, 0.f, 0.f});
+      for (int i = 1; i < 4; ++i) sb = mfma16x16x32(xf[mt][i], ones, sb);
+      for (int rt = 0; rt < RTX; ++rt)
+        for (int i = 0; i < 4; ++i) u[mt][rt] = mfma16x16x32(xf[mt][i], af[rt][i], u[mt][rt]);
+      ssum[mt] += sb;
+      // every column of the ones-product holds the row sum; column 0 stores it
+      if (c16 == 0) {
+        const int t = t0 + 16 * mt + 4 * q;
+        *reinterpret_cast<f32x4*>(p.sblk + (size_t)blk * p.Tp + t) = sb;
+      }
+    }
+  }
+
+  // In-workgroup reduction over the four waves (fixed order).
+  for (int mt = 0; mt < MT; ++mt) {
+    for (int rt = 0; rt < RTX; ++rt)
+      for (int v = 0; v < 4; ++v) red[wave][mt][rt][v][lane] = u[mt][rt][v];
+    for (int v = 0; v < 4; ++v) red[wave][mt][RTX][v][lane] = ssum[mt][v];
+  }
+  __syncthreads();
+  constexpr int kElems = MT * (RTX + 1) * 4 * 64;
+  const int R1 = p.r + 1;
+  for (int e = threadIdx.x; e < kElems; e += 256) {
+    const int l = e & 63, v = (e >> 6) & 3, rt = (e >> 8) % (RTX + 1), mt = (e >> 8) / (RTX + 1);
+    const float s = red[0][mt][rt][v][l] + red[1][mt][rt][v][l] + red[2][mt][rt][v][l] +
+                    red[3][mt][rt][v][l];
+    const int t = t0 + 16 * mt + 4 * (l >> 4) + v;
+    if (t >= p.T) continue;
+    if (rt < RTX) {
+      p.upart[((size_t)split * p.T + t) * R1 + 16 * rt + (l & 15)] = s;
+    } else if ((l & 15) == 0) {
+      p.upart[((size_t)split * p.T + t) * R1 + p.r] = s;
+    }
+  }
+
+  // Last workgroup of this token tile reduces the split partials.
+  __threadfence();
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const int prev = atomicAdd(&p.counters[tile], 1);
+    s_last = (prev == p.splits - 1);
+  }
+  __syncthreads();
+  if (!s_last) return;
+  __threadfence();
+  const int tcount = min(kProjTokens, p.T - t0);
+  for (int e = threadIdx.x; e < tcount * R1; e += 256) {
+    const int tt = e / R1, j = e % R1, t = t0 + tt;
+    float acc = 0.f;
+    for (int s = 0; s < p.splits; ++s) acc += p.upart[((size_t)s * p.T + t) * R1 + j];
+    if (j == p.r) {
+      p.stot[t] = acc;
+    } else {
+      const float gate = sigmoidf_safe(fmaf(p.gv[j], acc, p.bv[j]));
+      const float wv = p.alpha * (gate * acc);
+      p.wv32[(size_t)t * p.r + j] = wv;
+      const uint32_t hi = f32_to_bf16_rne(wv);
+      const uint32_t lo = f32_to_bf16_rne(wv - __uint_as_float(hi << 16));
+      p.wvhi[(size_t)t * p.r + j] = (uint16_t)hi;
+      p.wvlo[(size_t)t * p.r + j] = (uint16_t)lo;
+    }
+  }
+  if (threadIdx.x == 0) p.counters[tile] = 0;
+}
+
+template <int RTX>
+hipError_t launch_rtx(const ProjParams& p, dim3 grid, hipStream_t st) {
+  hipLaunchKernelGGL(projection_kernel<RTX>, grid, dim3(256), 0, st, p);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_projection(const Shape& s, const LayerArgs& a, const WsPtrs& w,
+                             hipStream_t st) {
+  const ProjPlan pl = plan_projection(s);
+  ProjParams p;
+  p.x = static_cast<const uint16_t*>(a.x);
+  p.A = static_cast<const uint16_t*>(a.A);
+  p.gv = a.gv;
+  p.bv = a.bv;
+  p.alpha = a.alpha;
+  p.upart = w.upart;
+  p.sblk = w.sblk;
+  p.stot = w.stot;
+  p.wv32 = w.wv32;
+  p.wvhi = w.wvhi;
+  p.wvlo = w.wvlo;
+  p.counters = w.counters + kProjCounterBase;
+  p.T = s.T;
+  p.K = s.K;
+  p.r = s.r;
+  p.Tp = pl.tiles * kProjTokens;
+  p.splits = pl.splits;
+  const dim3 grid(pl.tiles, pl.splits);
+  switch (s.r / 16) {
+    case 0: return launch_rtx<0>(p, grid, st);
+    case 1: return launch_rtx<1>(p, grid, st);
+    case 2: return launch_rtx<2>(p, grid, st);
+    case 3: return launch_rtx<3>(p, grid, st);
+    case 4: return launch_rtx<4>(p, grid, st);
+    case 5: return launch_rtx<5>(p, grid, st);
+    case 6: return launch_rtx<6>(p, grid, st);
+    case 7: return launch_rtx<7>(p, grid, st);
+    case 8: return launch_rtx<8>(p, grid, st);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace spear
