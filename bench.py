@@ -1,0 +1,286 @@
+"""Benchmark of the error-compensated W4 linear layer on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config c3]
+
+Default workload (config c3): the 70B-shaped MLP down-projection
+(d_in = 28672, d_out = 8192, int4 group-wise g = 128 asymmetric with fp16
+scales and int4 zero-points, compensator rank 64).  One step is the mixed
+phase of chunked-prefill serving: a 16-token decode batch and a 512-token
+prefill chunk, both through the phase-aware dispatcher (spear_ec_linear), on
+one stream.  Decode runs first, so it streams its weights from HBM; weights
+rotate over several copies so no call finds them in the 256 MB last-level
+cache from an earlier step.  Inputs are seeded synthetic tensors of the
+workload's shapes and distributions, resident in HBM before timing starts.
+
+Reported (one JSON line):
+  value        decode effective bandwidth: algorithmic bytes of the decode
+               call / its duration (GB/s); prefill TFLOP/s alongside.
+  roofline     for the dominant call (prefill, matrix cores) and, under
+               roofline_decode, for the decode call (HBM).
+  cpu_baseline the single-threaded fp64 oracle on a row slice of the same
+               layer (all tokens, a subset of output rows), scaled to GB/s.
+
+Algorithmic bytes of a call = packed weights + scales + zeros + A + B + g + b
++ x + y, each once.  Algorithmic flops = 2TKN + 2Tr(K + N) + 4Tr.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "decode: effective HBM GB/s (% peak); prefill: TFLOP/s (% MFMA peak)"
+HBM_PEAK_GBS = 8000.0
+BF16_PEAK_TFLOPS = 2500.0
+
+
+def layer_bytes(K, N, r, g, asym, T):
+    G = K // g
+    w = N * K // 2 + N * G * 2 + (N * ((G + 7) // 8) * 4 if asym else 0)
+    comp = r * K * 2 + N * r * 2 + 2 * r * 4
+    return w + comp + T * K * 2 + T * N * 2
+
+
+def weight_bytes(K, N, r, g, asym):
+    G = K // g
+    return N * K // 2 + N * G * 2 + (N * ((G + 7) // 8) * 4 if asym else 0) + r * K * 2 + N * r * 2
+
+
+def layer_flops(K, N, r, T):
+    return 2 * T * K * N + 2 * T * r * (K + N) + 4 * T * r
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "quantization_error_compensation_amd", "csrc")
+    for f in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, f), "rb") as fh:
+            h.update(f.encode() + fh.read())
+    return h.hexdigest()[:16]
+
+
+WORKLOADS = {
+    "c3": dict(steps=[("decode", 16), ("prefill", 512)],
+               text="70B MLP down-projection d_in=28672 d_out=8192, int4 g=128 asymmetric "
+                    "(fp16 scales, int4 zero-points), rank 64; mixed step = 16-token decode + "
+                    "512-token prefill chunk through the dispatcher"),
+    "c1": dict(steps=[("decode", 1), ("decode", 8), ("decode", 32)],
+               text="7B attention projection d_in=d_out=4096, int4 g=128 asymmetric, rank 32; "
+                    "decode batches of 1, 8 and 32 tokens"),
+    "c2": dict(steps=[("prefill", 2048)],
+               text="7B MLP up-projection d_in=4096 d_out=11008, int4 symmetric per-channel, "
+                    "rank 64; 2048-token prefill"),
+    "c4": dict(steps=[("decode", 1), ("decode", 16), ("prefill", 256), ("prefill", 4096)],
+               text="d_in=d_out=8192 sweep point, int4 symmetric per-channel, rank 128; tokens "
+                    "1, 16, 256, 4096"),
+}
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--config", default="c3", choices=sorted(WORKLOADS))
+    ap.add_argument("--rank", type=int, default=None, help="override the compensator rank")
+    ap.add_argument("--copies", type=int, default=0, help="weight copies to rotate (0 = auto)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run one plain device copy of known size (for HBM counter scaling)")
+    return ap.parse_args()
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(run with --gpus 1).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import quantization_error_compensation_amd as q
+    import synth
+
+    sys.path.insert(0, os.path.join(ROOT, "tests"))
+    from helpers import to_dev_bf16, to_dev_f32
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    q.load_library()
+
+    spec = synth.CONFIGS[args.config]
+    K, N, g, asym = spec.d_in, spec.d_out, spec.group_size, spec.asym
+    r = spec.rank if args.rank is None else args.rank
+    plan = WORKLOADS[args.config]["steps"]
+    Tmax = max(T for _, T in plan)
+    Ttot = sum(T for _, T in plan)
+
+    t_setup = time.time()
+    W = synth.weights(spec)
+    X = synth.activations(spec, Ttot)
+    A, B, gv, bv = synth.compensator(spec, r)
+    desc = q.make_desc(K, N, r, g, asym)
+    wq0, sc0, zs0 = q.alloc_packed(desc, dev)
+    q.spear_ec_quantize_rtn(desc, to_dev_f32(W, dev), wq0, sc0, zs0)
+    torch.cuda.synchronize()
+    del W
+    wbytes = weight_bytes(K, N, r, g, asym)
+    copies = args.copies or max(2, int(np.ceil(1.0e9 / wbytes)))
+    layers = []
+    for c in range(copies):
+        layers.append(dict(
+            wq=wq0.clone(), sc=sc0.clone(), zs=zs0.clone() if zs0 is not None else None,
+            A=to_dev_bf16(A, dev) if r else None, B=to_dev_bf16(B, dev) if r else None,
+            g=to_dev_f32(gv, dev) if r else None, b=to_dev_f32(bv, dev) if r else None))
+    xs, ys, off = [], [], 0
+    for _, T in plan:
+        xs.append(to_dev_bf16(X[off:off + T], dev))
+        ys.append(torch.empty((T, N), dtype=torch.bfloat16, device=dev))
+        off += T
+    ws = q.alloc_workspace(desc, Tmax, dev)
+    torch.cuda.synchronize()
+    setup_s = time.time() - t_setup
+
+    stream = torch.cuda.current_stream()
+
+    def step(i, evs=None):
+        L = layers[i % copies]
+        for j, (path, T) in enumerate(plan):
+            if evs is not None:
+                evs[j].record(stream)
+            q.spear_ec_linear(desc, xs[j], L["wq"], L["sc"], L["zs"], L["A"], L["B"], L["g"],
+                              L["b"], spec.alpha, ys[j], ws, stream)
+        if evs is not None:
+            evs[len(plan)].record(stream)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    n = len(plan)
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(n + 1)] for _ in range(args.steps)]
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record(stream)
+    for i in range(args.steps):
+        step(args.warmup + i, evs[i])
+    end.record(stream)
+    torch.cuda.synchronize()
+    ms_total = start.elapsed_time(end)
+    ms_step = ms_total / args.steps
+    per_call_ms = [float(np.mean([evs[i][j].elapsed_time(evs[i][j + 1]) for i in range(args.steps)]))
+                   for j in range(n)]
+
+    calls = []
+    for j, (path, T) in enumerate(plan):
+        by = layer_bytes(K, N, r, g, asym, T)
+        fl = layer_flops(K, N, r, T)
+        s = per_call_ms[j] / 1e3
+        calls.append(dict(path=path, tokens=T, ms=per_call_ms[j], bytes=by, flops=fl,
+                          gbs=by / s / 1e9, tflops=fl / s / 1e12))
+
+    if args.copy_calibration:
+        a = torch.empty(1 << 28, dtype=torch.uint8, device=dev)   # 256 MiB
+        b = torch.empty_like(a)
+        b.copy_(a)
+        torch.cuda.synchronize()
+
+    dec = [c for c in calls if c["path"] == "decode"]
+    pre = [c for c in calls if c["path"] == "prefill"]
+    dominant = max(calls, key=lambda c: c["ms"])
+    traffic = load_traffic(args.config)
+
+    def roof(c):
+        if c["path"] == "decode":
+            return {"bound": "hbm", "achieved": round(c["gbs"], 1), "peak": HBM_PEAK_GBS,
+                    "unit": "GB/s", "frac": round(c["gbs"] / HBM_PEAK_GBS, 4),
+                    "traffic": traffic.get(f"decode_T{c['tokens']}"),
+                    "kernel": f"spear_ec_linear (decode, {c['tokens']} tokens): projection + decode kernels",
+                    "avg_us": round(c["ms"] * 1e3, 2)}
+        return {"bound": "mfma", "achieved": round(c["tflops"], 1), "peak": BF16_PEAK_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(c["tflops"] / BF16_PEAK_TFLOPS, 4),
+                "traffic": traffic.get(f"prefill_T{c['tokens']}"),
+                "kernel": f"spear_ec_linear (prefill, {c['tokens']} tokens): projection + prefill kernels",
+                "avg_us": round(c["ms"] * 1e3, 2)}
+
+    head = dec[0] if dec else pre[0]
+    value = head["gbs"] if dec else head["tflops"]
+    unit = "GB/s" if dec else "TFLOP/s"
+    out = {
+        "metric": METRIC, "value": round(value, 2), "unit": unit, "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": f"{args.config}: " + WORKLOADS[args.config]["text"],
+                   "d_in": K, "d_out": N, "rank": r, "group_size": g,
+                   "zero_points": asym, "tokens_per_step": [T for _, T in plan],
+                   "weight_copies_rotated": copies, "parallelism": "single GPU"},
+        "calls": [{k: (round(v, 4) if isinstance(v, float) else v) for k, v in c.items()}
+                  for c in calls],
+        "roofline": roof(dominant),
+    }
+    if dec and pre:
+        out["prefill"] = {"value": round(pre[0]["tflops"], 2), "unit": "TFLOP/s",
+                          "frac_of_peak": round(pre[0]["tflops"] / BF16_PEAK_TFLOPS, 4)}
+        out["roofline_decode"] = roof(dec[0])
+    out["kernel_source_hash"] = kernel_source_hash()
+    out["setup_s"] = round(setup_s, 1)
+
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(spec, r, plan, X, A, B, gv, bv, unit)
+    print(json.dumps(out), flush=True)
+
+
+def load_traffic(config):
+    """HBM traffic per call measured with rocprofv3 counters, if it was taken
+    on the current kernel sources (profiles/traffic_<config>.json)."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{config}.json")
+    if not os.path.exists(path):
+        return {}
+    with open(path) as f:
+        t = json.load(f)
+    if t.get("kernel_source_hash") != kernel_source_hash():
+        return {}
+    return t.get("bytes_per_call", {})
+
+
+def cpu_baseline(spec, r, plan, X, A, B, gv, bv, unit):
+    """The fp64 oracle on a bounded sample of the same layer: every token of
+    the first call of the step, a slice of output rows.  Scaled to the unit
+    of `value` by the algorithmic bytes (or flops) of that slice."""
+    import oracle
+    K, N, g, asym = spec.d_in, spec.d_out, spec.group_size, spec.asym
+    path, T = plan[0]
+    x = X[:T]
+    # the slice: a few seconds of single-core work
+    rows = max(16, min(N, int(6.0e9 / max(1, T * K))))
+    import synth
+    Wsl = synth.weights(spec, rows=rows)
+    t0 = time.time()
+    wq, sc, zs = oracle.quantize_rtn(Wsl, g, asym)
+    t1 = time.time()
+    oracle.forward(x, wq, sc, zs, A if r else None, B[:rows] if r else None, gv, bv, spec.alpha, g)
+    t2 = time.time()
+    secs = t2 - t1
+    by = layer_bytes(K, rows, r, g, asym, T)
+    fl = layer_flops(K, rows, r, T)
+    val = by / secs / 1e9 if unit == "GB/s" else fl / secs / 1e12
+    return {"value": round(val, 6), "unit": unit, "cores": 1, "kind": "oracle",
+            "sample": f"{path} call, all {T} tokens x first {rows} of {N} output rows "
+                      f"(compensator for all tokens); forward {secs:.1f} s, quantize {t1 - t0:.1f} s"}
+
+
+if __name__ == "__main__":
+    main()

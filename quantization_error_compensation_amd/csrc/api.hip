@@ -6,7 +6,7 @@
 
 #include <algorithm>
 
-#include "../../include/spear_ec.h"
+#include "spear_ec.h"
 #include "internal.hpp"
 
 namespace spear {
@@ -30,30 +30,40 @@ ProjPlan plan_projection(const Shape& s) {
 DecodePlan plan_decode(const Shape& s) {
   DecodePlan pl;
   pl.bands = (s.N + kDecodeBandRows - 1) / kDecodeBandRows;
+  pl.rank_bands = s.r / 16;
   const int KB = s.KB();
-  const int want = (512 + pl.bands - 1) / pl.bands;
-  pl.splits = std::max(1, std::min(want, KB / 4));
+  const int want = (512 + pl.bands - 1) / pl.bands;   // about two workgroups per CU
+  pl.splits = std::max(1, std::min(want, KB / 4));     // at least one block per wave
   return pl;
 }
 
 static size_t up256(size_t v) { return (v + 255) & ~(size_t)255; }
 
 Workspace layout(const Shape& s, bool decode) {
-  const ProjPlan pp = plan_projection(s);
-  const size_t T = (size_t)s.T, r = (size_t)s.r, Tp = (size_t)pp.tiles * kProjTokens;
+  const size_t T = (size_t)s.T, r = (size_t)s.r;
   Workspace w;
   size_t o = 0;
   w.counters = o; o = up256(o + sizeof(int) * kCounterSlots);
   w.wv32 = o;     o = up256(o + sizeof(float) * T * r);
-  w.wvhi = o;     o = up256(o + 2 * T * r);
-  w.wvlo = o;     o = up256(o + 2 * T * r);
-  w.sblk = o;     o = up256(o + sizeof(float) * (size_t)s.KB() * Tp);
-  w.stot = o;     o = up256(o + sizeof(float) * Tp);
-  w.upart = o;    o = up256(o + sizeof(float) * (size_t)pp.splits * T * (r + 1));
-  w.ypart = o;
   if (decode) {
     const DecodePlan dp = plan_decode(s);
-    o = up256(o + sizeof(float) * (size_t)dp.splits * T * (size_t)s.N);
+    w.wvhi = w.wvlo = w.sblk = w.stot = o;
+    w.upart = o;  o = up256(o + sizeof(float) * (size_t)dp.splits * T * r);
+    w.ypart = o;  o = up256(o + sizeof(float) * (size_t)dp.splits * T * (size_t)s.N);
+  } else {
+    const ProjPlan pp = plan_projection(s);
+    const size_t Tp = (size_t)pp.tiles * kProjTokens;
+    w.wvhi = o;   o = up256(o + 2 * T * r);
+    w.wvlo = o;   o = up256(o + 2 * T * r);
+    w.sblk = o;   o = up256(o + sizeof(float) * (size_t)s.KB() * Tp);
+    w.stot = o;   o = up256(o + sizeof(float) * Tp);
+    // splits * T <= min(max(1, KB/4) * T, 16384 + T): a bound that grows with
+    // T, so sizing for the largest token count covers every smaller one.
+    const size_t kb4 = (size_t)std::max(1, s.KB() / 4);
+    const size_t parts = std::min(kb4 * T, (size_t)16384 + T);
+    (void)pp;
+    w.upart = o;  o = up256(o + sizeof(float) * parts * (r + 1));
+    w.ypart = o;
   }
   w.total = o;
   return w;
@@ -152,9 +162,9 @@ static int linear(Path path, const spear_ec_desc* d, int32_t tokens, const void*
   a.alpha = alpha;
   a.y = y;
   const WsPtrs wp = carve(workspace, wl);
+  if (decode) return hip_status(launch_decode(s, a, wp, stream), "decode kernel launch");
   rc = hip_status(launch_projection(s, a, wp, stream), "projection kernel launch");
   if (rc) return rc;
-  if (decode) return hip_status(launch_decode(s, a, wp, stream), "decode kernel launch");
   return hip_status(launch_prefill(s, a, wp, stream), "prefill kernel launch");
 }
 

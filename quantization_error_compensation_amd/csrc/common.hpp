@@ -12,9 +12,9 @@
 // the weight side, so the dequantized weight the layer sees is the exact
 // (c - z) * s of the format.
 //
-// K order.  The pairs built from a word hold columns (0,4), (1,5), (2,6),
-// (3,7) of its eight, so a matrix-core operand carries the columns of an
-// 8-column block in the order 0,4,1,5,2,6,3,7.  A dot product does not depend
+// K order.  The pairs built from a word hold columns (0,2), (4,6), (1,3),
+// (5,7) of its eight, so a matrix-core operand carries the columns of an
+// 8-column block in the order 0,2,4,6,1,3,5,7.  A dot product does not depend
 // on the order of its terms, so the activations are permuted the same way
 // (x_permute8) and the packed weights keep their canonical layout.
 #pragma once
@@ -34,25 +34,28 @@ constexpr uint32_t kBf16Offset128 = 0x43004300u;  // bf16 pair (128.0, 128.0)
 constexpr uint32_t kBf16One = 0x3F803F80u;        // bf16 pair (1.0, 1.0)
 
 // Eight codes (nibble j = column j of the block) -> bf16 pairs of 128 + c in
-// the operand order 0,4,1,5,2,6,3,7.
+// the operand order 0,2,4,6,1,3,5,7: the even and odd nibbles are split into
+// bytes, and v_perm_b32 places each byte under the bf16 exponent byte 0x43.
 __device__ __forceinline__ u32x4 codes_to_bf16_offset(uint32_t w) {
-  const uint32_t m = 0x000F000Fu;
+  const uint32_t lo = w & 0x0F0F0F0Fu;          // bytes: c0 c2 c4 c6
+  const uint32_t hi = (w >> 4) & 0x0F0F0F0Fu;   // bytes: c1 c3 c5 c7
+  const uint32_t m = 0x43434343u;
   u32x4 o;
-  o.x = (w & m) | kBf16Offset128;
-  o.y = ((w >> 4) & m) | kBf16Offset128;
-  o.z = ((w >> 8) & m) | kBf16Offset128;
-  o.w = ((w >> 12) & m) | kBf16Offset128;
+  o.x = __builtin_amdgcn_perm(lo, m, 0x01050004u);  // (c0, c2)
+  o.y = __builtin_amdgcn_perm(lo, m, 0x01070006u);  // (c4, c6)
+  o.z = __builtin_amdgcn_perm(hi, m, 0x01050004u);  // (c1, c3)
+  o.w = __builtin_amdgcn_perm(hi, m, 0x01070006u);  // (c5, c7)
   return o;
 }
 
 // Eight consecutive bf16 activations (packed in 4 words) -> the same operand
-// order 0,4,1,5,2,6,3,7 as codes_to_bf16_offset.
+// order 0,2,4,6,1,3,5,7 as codes_to_bf16_offset.
 __device__ __forceinline__ u32x4 x_permute8(u32x4 d) {
   u32x4 o;
-  o.x = (d.x & 0xFFFFu) | (d.z << 16);
-  o.y = (d.x >> 16) | (d.z & 0xFFFF0000u);
-  o.z = (d.y & 0xFFFFu) | (d.w << 16);
-  o.w = (d.y >> 16) | (d.w & 0xFFFF0000u);
+  o.x = __builtin_amdgcn_perm(d.y, d.x, 0x05040100u);  // (x0, x2)
+  o.y = __builtin_amdgcn_perm(d.w, d.z, 0x05040100u);  // (x4, x6)
+  o.z = __builtin_amdgcn_perm(d.y, d.x, 0x07060302u);  // (x1, x3)
+  o.w = __builtin_amdgcn_perm(d.w, d.z, 0x07060302u);  // (x5, x7)
   return o;
 }
 
@@ -86,6 +89,45 @@ __device__ __forceinline__ float sigmoidf_safe(float z) {
   if (z >= 0.f) return 1.f / (1.f + expf(-z));
   const float e = expf(z);
   return e / (1.f + e);
+}
+
+// Cross-workgroup data without cache-wide fences.  A release fence writes the
+// whole XCD L2 back and an acquire invalidates it; done by every workgroup they
+// stall the streaming ones.  Data that one workgroup hands to another is
+// instead stored and loaded at device scope (sc1: coherent across XCDs, no
+// L2-wide maintenance), and the writer waits for its stores to complete
+// before it bumps the arrival counter.
+__device__ __forceinline__ void store_dev(float* p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float load_dev(const float* p) {
+  return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ int load_dev(const int* p) {
+  return __hip_atomic_load(const_cast<int*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void store_dev(int* p, int v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// Wait until every memory operation this wave issued has completed.
+__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0); }
+
+// Raw buffer resource over [base, base + bytes): loads at offsets past the end
+// return zero, which masks rows past d_out and tokens past T.  Offsets are
+// 32-bit; every resource here spans at most one band of rows or one operand.
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+__device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
+                                           0x00020000);
+}
+__device__ __forceinline__ u32x4 bload16(rsrc_t r, uint32_t voff, uint32_t soff) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
+}
+__device__ __forceinline__ uint32_t bload4(rsrc_t r, uint32_t voff, uint32_t soff) {
+  return (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0);
+}
+__device__ __forceinline__ uint32_t bload2(rsrc_t r, uint32_t voff, uint32_t soff) {
+  return (uint32_t)(uint16_t)__builtin_amdgcn_raw_buffer_load_b16(r, voff, soff, 0);
 }
 
 __device__ __forceinline__ u32x4 load16(const void* p) {

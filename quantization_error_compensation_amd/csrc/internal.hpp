@@ -10,12 +10,19 @@ namespace spear {
 
 constexpr int kBlockK = 128;          // K block: one scale group (g = 128) or a slice of a row
 constexpr int kDecodeBandRows = 64;   // output rows per decode workgroup
-constexpr int kProjTokens = 32;       // tokens per projection workgroup
+constexpr int kProjTokens = 32;       // tokens per projection workgroup (prefill path)
 constexpr int kPrefillBM = 128;       // tokens per prefill tile
 constexpr int kPrefillBN = 128;       // output rows per prefill tile
-constexpr int kCounterSlots = 16384;  // int32 arrival counters at the head of the workspace
-constexpr int kProjCounterBase = 0;   // [0, 8192): projection, one per token tile
-constexpr int kDecodeCounterBase = 8192;  // [8192, 16384): decode, one per row band
+constexpr int kCounterSlots = 4096;   // int32 words at the head of the workspace
+
+// Decode counter words (all zero between calls).
+constexpr int kCtrTicket = 0;    // workgroup tickets
+constexpr int kCtrRankDone = 1;  // rank bands whose gated projection is published
+constexpr int kCtrExit = 2;      // workgroups that have finished
+constexpr int kCtrError = 3;     // set to 1 if a workgroup saw an inconsistent workspace
+constexpr int kCtrRankBand = 16;   // [16, 24): arrivals per rank band
+constexpr int kCtrRowBand = 64;    // [64, 64 + bands): arrivals per row band
+constexpr int kMaxRowBands = kCounterSlots - kCtrRowBand;
 
 struct Shape {
   int K, N, r, g, T;
@@ -24,16 +31,18 @@ struct Shape {
   int KB() const { return K / kBlockK; }
 };
 
-// Work split of the rank-r projection for T tokens.
+// Work split of the rank-r projection (prefill path) for T tokens.
 struct ProjPlan {
   int tiles;   // token tiles of kProjTokens
   int splits;  // K splits
 };
 
-// Work split of the decode GEMV.
+// Work split of the fused decode kernel.
 struct DecodePlan {
-  int bands;   // N / 64 (rounded up)
-  int splits;  // K splits across workgroups
+  int bands;       // 64-row output bands
+  int splits;      // K splits across workgroups
+  int rank_bands;  // 16-row bands of A
+  int workgroups() const { return (bands + rank_bands) * splits; }
 };
 
 ProjPlan plan_projection(const Shape& s);
@@ -49,11 +58,11 @@ Workspace layout(const Shape& s, bool decode);
 struct WsPtrs {
   int* counters;
   float* wv32;     // [T][r]      alpha * gated projection
-  uint16_t* wvhi;  // [T][r]      bf16 high part of alpha * v
-  uint16_t* wvlo;  // [T][r]      bf16 remainder
-  float* sblk;     // [KB][T]     sum of x over each 128-column block
-  float* stot;     // [T]         sum of x over the whole row
-  float* upart;    // [splits][T][r + 1] projection partials (+ row-sum partial)
+  uint16_t* wvhi;  // [T][r]      bf16 high part of alpha * v (prefill)
+  uint16_t* wvlo;  // [T][r]      bf16 remainder (prefill)
+  float* sblk;     // [KB][Tp]    sum of x over each 128-column block (prefill)
+  float* stot;     // [T]         sum of x over the whole row (prefill)
+  float* upart;    // projection partials: prefill [splits][T][r+1], decode [splits][T][r]
   float* ypart;    // [splits][T][N] decode partials
 };
 WsPtrs carve(void* base, const Workspace& w);

@@ -1,17 +1,19 @@
-// Rank-r projection and gate of the error compensator, once per token.
+// Rank-r projection and gate of the error compensator for the prefill path.
 //
 // SPEAR summary, section 2.1 A (input-adaptive error compensators): the
 // compensator projects the activation x into a low-rank space with A and
-// gates each token's projection.  This kernel computes, for every token,
-//     u[t,j] = sum_k A[j,k] x[t,k]                 (matrix cores, fp32 acc)
+// gates each token's projection.  For a prefill batch this is a small GEMM
+// (r/N of the main one), computed once per token:
+//     u[t,j]  = sum_k A[j,k] x[t,k]                   (matrix cores, fp32 acc)
 //     wv[t,j] = alpha * sigmoid(g[j] u[t,j] + b[j]) * u[t,j]
-// plus the per-128-column sums of x that the main kernels use to remove the
-// +128 offset of their integer-code operands, and the whole-row sums.
+// together with the per-128-column sums of x, which the prefill GEMM uses to
+// remove the +128 offset of its integer-code operands, and whole-row sums.
 //
-// Work split: one workgroup per (32-token tile, K split).  The four waves of a
-// workgroup take contiguous runs of 128-column blocks; partial u of the split
-// goes to the workspace and the last workgroup to arrive for a token tile sums
-// the partials in split order (deterministic), applies the gate and publishes.
+// projection_kernel: one workgroup per (32-token tile, K split); the four
+// waves take contiguous runs of 128-column blocks; the split's partial u (and
+// row sum) goes to the workspace.  finish_kernel: one thread per (token, j)
+// sums the split partials in split order (deterministic), applies the gate
+// and writes alpha * v in fp32 and as a bf16 high/low pair.
 #include "common.hpp"
 #include "internal.hpp"
 
@@ -30,16 +32,14 @@ struct ProjParams {
   float* wv32;         // [T][r]
   uint16_t* wvhi;      // [T][r]
   uint16_t* wvlo;      // [T][r]
-  int* counters;       // one per token tile
   int T, K, r, Tp, splits;
 };
 
 template <int RTX>  // RTX = r / 16 rank tiles
 __global__ __launch_bounds__(256, 2) void projection_kernel(ProjParams p) {
-  constexpr int MT = 2;  // 32 tokens per workgroup = two 16-row MFMA tiles
+  constexpr int MT = 2;                  // 32 tokens = two 16-row MFMA tiles
   constexpr int RA = RTX > 0 ? RTX : 1;  // array extent (rank 0 still sums x)
   __shared__ float red[4][MT][RTX + 1][4][64];
-  __shared__ int s_last;
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int q = lane >> 4, c16 = lane & 15;
@@ -52,12 +52,8 @@ __global__ __launch_bounds__(256, 2) void projection_kernel(ProjParams p) {
   const int t0 = tile * kProjTokens;
 
   const uint16_t* xr[MT];
-  bool tok_ok[MT];
-  for (int mt = 0; mt < MT; ++mt) {
-    const int t = t0 + 16 * mt + c16;
-    tok_ok[mt] = t < p.T;
-    xr[mt] = p.x + (size_t)(tok_ok[mt] ? t : 0) * p.K + 32 * q;
-  }
+  for (int mt = 0; mt < MT; ++mt)  // clamped: rows past T are computed but never stored
+    xr[mt] = p.x + (size_t)min(t0 + 16 * mt + c16, p.T - 1) * p.K + 32 * q;
   const uint16_t* ar[RA];
   for (int rt = 0; rt < RTX; ++rt) ar[rt] = p.A + (size_t)(16 * rt + c16) * p.K + 32 * q;
 
@@ -72,8 +68,7 @@ __global__ __launch_bounds__(256, 2) void projection_kernel(ProjParams p) {
   for (int blk = wb0; blk < wb1; ++blk) {
     u32x4 xf[MT][4], af[RA][4];
     for (int mt = 0; mt < MT; ++mt)
-      for (int i = 0; i < 4; ++i)
-        xf[mt][i] = tok_ok[mt] ? load16(xr[mt] + (size_t)blk * kBlockK + 8 * i) : u32x4{0, 0, 0, 0};
+      for (int i = 0; i < 4; ++i) xf[mt][i] = load16(xr[mt] + (size_t)blk * kBlockK + 8 * i);
     for (int rt = 0; rt < RTX; ++rt)
       for (int i = 0; i < 4; ++i) af[rt][i] = load16(ar[rt] + (size_t)blk * kBlockK + 8 * i);
     for (int mt = 0; mt < MT; ++mt) {
@@ -85,7 +80,10 @@ __global__ __launch_bounds__(256, 2) void projection_kernel(ProjParams p) {
       // every column of the ones-product holds the row sum; column 0 stores it
       if (c16 == 0) {
         const int t = t0 + 16 * mt + 4 * q;
-        *reinterpret_cast<f32x4*>(p.sblk + (size_t)blk * p.Tp + t) = sb;
+        f32x4 sv = sb;
+        for (int v = 0; v < 4; ++v)
+          if (t + v >= p.T) sv[v] = 0.f;
+        *reinterpret_cast<f32x4*>(p.sblk + (size_t)blk * p.Tp + t) = sv;
       }
     }
   }
@@ -111,35 +109,27 @@ __global__ __launch_bounds__(256, 2) void projection_kernel(ProjParams p) {
       p.upart[((size_t)split * p.T + t) * R1 + p.r] = s;
     }
   }
+}
 
-  // Last workgroup of this token tile reduces the split partials.
-  __threadfence();
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    const int prev = atomicAdd(&p.counters[tile], 1);
-    s_last = (prev == p.splits - 1);
+__global__ __launch_bounds__(256) void finish_kernel(ProjParams p) {
+  const int R1 = p.r + 1;
+  const int e = blockIdx.x * 256 + threadIdx.x;
+  if (e >= p.T * R1) return;
+  const int t = e / R1, j = e % R1;
+  float acc = 0.f;
+#pragma unroll 8
+  for (int s = 0; s < p.splits; ++s) acc += p.upart[((size_t)s * p.T + t) * R1 + j];
+  if (j == p.r) {
+    p.stot[t] = acc;
+    return;
   }
-  __syncthreads();
-  if (!s_last) return;
-  __threadfence();
-  const int tcount = min(kProjTokens, p.T - t0);
-  for (int e = threadIdx.x; e < tcount * R1; e += 256) {
-    const int tt = e / R1, j = e % R1, t = t0 + tt;
-    float acc = 0.f;
-    for (int s = 0; s < p.splits; ++s) acc += p.upart[((size_t)s * p.T + t) * R1 + j];
-    if (j == p.r) {
-      p.stot[t] = acc;
-    } else {
-      const float gate = sigmoidf_safe(fmaf(p.gv[j], acc, p.bv[j]));
-      const float wv = p.alpha * (gate * acc);
-      p.wv32[(size_t)t * p.r + j] = wv;
-      const uint32_t hi = f32_to_bf16_rne(wv);
-      const uint32_t lo = f32_to_bf16_rne(wv - __uint_as_float(hi << 16));
-      p.wvhi[(size_t)t * p.r + j] = (uint16_t)hi;
-      p.wvlo[(size_t)t * p.r + j] = (uint16_t)lo;
-    }
-  }
-  if (threadIdx.x == 0) p.counters[tile] = 0;
+  const float gate = sigmoidf_safe(fmaf(p.gv[j], acc, p.bv[j]));
+  const float wv = p.alpha * (gate * acc);
+  p.wv32[(size_t)t * p.r + j] = wv;
+  const uint32_t hi = f32_to_bf16_rne(wv);
+  const uint32_t lo = f32_to_bf16_rne(wv - __uint_as_float(hi << 16));
+  p.wvhi[(size_t)t * p.r + j] = (uint16_t)hi;
+  p.wvlo[(size_t)t * p.r + j] = (uint16_t)lo;
 }
 
 template <int RTX>
@@ -165,25 +155,29 @@ hipError_t launch_projection(const Shape& s, const LayerArgs& a, const WsPtrs& w
   p.wv32 = w.wv32;
   p.wvhi = w.wvhi;
   p.wvlo = w.wvlo;
-  p.counters = w.counters + kProjCounterBase;
   p.T = s.T;
   p.K = s.K;
   p.r = s.r;
   p.Tp = pl.tiles * kProjTokens;
   p.splits = pl.splits;
   const dim3 grid(pl.tiles, pl.splits);
+  hipError_t e;
   switch (s.r / 16) {
-    case 0: return launch_rtx<0>(p, grid, st);
-    case 1: return launch_rtx<1>(p, grid, st);
-    case 2: return launch_rtx<2>(p, grid, st);
-    case 3: return launch_rtx<3>(p, grid, st);
-    case 4: return launch_rtx<4>(p, grid, st);
-    case 5: return launch_rtx<5>(p, grid, st);
-    case 6: return launch_rtx<6>(p, grid, st);
-    case 7: return launch_rtx<7>(p, grid, st);
-    case 8: return launch_rtx<8>(p, grid, st);
+    case 0: e = launch_rtx<0>(p, grid, st); break;
+    case 1: e = launch_rtx<1>(p, grid, st); break;
+    case 2: e = launch_rtx<2>(p, grid, st); break;
+    case 3: e = launch_rtx<3>(p, grid, st); break;
+    case 4: e = launch_rtx<4>(p, grid, st); break;
+    case 5: e = launch_rtx<5>(p, grid, st); break;
+    case 6: e = launch_rtx<6>(p, grid, st); break;
+    case 7: e = launch_rtx<7>(p, grid, st); break;
+    case 8: e = launch_rtx<8>(p, grid, st); break;
     default: return hipErrorInvalidValue;
   }
+  if (e != hipSuccess) return e;
+  const int elems = s.T * (s.r + 1);
+  hipLaunchKernelGGL(finish_kernel, dim3((elems + 255) / 256), dim3(256), 0, st, p);
+  return hipGetLastError();
 }
 
 }  // namespace spear

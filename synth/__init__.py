@@ -81,9 +81,10 @@ def _rng(spec: LayerSpec, tensor: int, salt: int = 0) -> np.random.Generator:
     return np.random.default_rng(spec.seed_base + tensor + 100000 * salt)
 
 
-def weights(spec: LayerSpec, salt: int = 0) -> np.ndarray:
-    """fp32 [d_out][d_in]."""
-    w = _rng(spec, TENSOR_W, salt).standard_normal((spec.d_out, spec.d_in))
+def weights(spec: LayerSpec, salt: int = 0, rows: int | None = None) -> np.ndarray:
+    """fp32 [d_out][d_in] (or its first `rows` rows: the same stream prefix)."""
+    n = spec.d_out if rows is None else rows
+    w = _rng(spec, TENSOR_W, salt).standard_normal((n, spec.d_in))
     return (w * spec.w_std).astype(np.float32)
 
 
