@@ -27,13 +27,23 @@ ProjPlan plan_projection(const Shape& s) {
   return pl;
 }
 
-DecodePlan plan_decode(const Shape& s) {
+DecodePlan plan_decode(const Shape& s, int slots) {
   DecodePlan pl;
+  const int KB = s.KB();
   pl.bands = (s.N + kDecodeBandRows - 1) / kDecodeBandRows;
   pl.rank_bands = s.r / 16;
-  const int KB = s.KB();
-  const int want = (512 + pl.bands - 1) / pl.bands;   // about two workgroups per CU
-  pl.splits = std::max(1, std::min(want, KB / 4));     // at least one block per wave
+  pl.units = (pl.bands + pl.rank_bands) * KB;
+  // At least 12 units (3 blocks per wave) per workgroup so the fixed latency of
+  // a workgroup is amortized; at most 128 units (32 blocks per wave, the size
+  // of the per-wave scale staging area).
+  auto wgs = [&](int sl) {
+    int P = std::min(sl, (pl.units + 11) / 12);
+    P = std::max(P, (pl.units + 127) / 128);
+    return std::max(1, std::min(P, pl.units));
+  };
+  pl.workgroups = wgs(std::min(std::max(slots, 1), kMaxSlots));
+  const int pmax = wgs(kMaxSlots);  // the partial-sum stride is sized for the bound
+  pl.maxseg = (KB + pl.units / pmax - 1) / (pl.units / pmax) + 1;
   return pl;
 }
 
@@ -46,10 +56,10 @@ Workspace layout(const Shape& s, bool decode) {
   w.counters = o; o = up256(o + sizeof(int) * kCounterSlots);
   w.wv32 = o;     o = up256(o + sizeof(float) * T * r);
   if (decode) {
-    const DecodePlan dp = plan_decode(s);
-    w.wvhi = w.wvlo = w.sblk = w.stot = o;
-    w.upart = o;  o = up256(o + sizeof(float) * (size_t)dp.splits * T * r);
-    w.ypart = o;  o = up256(o + sizeof(float) * (size_t)dp.splits * T * (size_t)s.N);
+    const DecodePlan dp = plan_decode(s, kMaxSlots);
+    w.wvhi = w.wvlo = w.sblk = w.stot = w.upart = o;
+    w.ypart = o;
+    o = up256(o + sizeof(float) * (size_t)(dp.bands + dp.rank_bands) * dp.maxseg * T * 64);
   } else {
     const ProjPlan pp = plan_projection(s);
     const size_t Tp = (size_t)pp.tiles * kProjTokens;

@@ -16,13 +16,11 @@ constexpr int kPrefillBN = 128;       // output rows per prefill tile
 constexpr int kCounterSlots = 4096;   // int32 words at the head of the workspace
 
 // Decode counter words (all zero between calls).
-constexpr int kCtrTicket = 0;    // workgroup tickets
 constexpr int kCtrRankDone = 1;  // rank bands whose gated projection is published
-constexpr int kCtrExit = 2;      // workgroups that have finished
+constexpr int kCtrExit = 2;      // decode workgroups that have finished
 constexpr int kCtrError = 3;     // set to 1 if a workgroup saw an inconsistent workspace
-constexpr int kCtrRankBand = 16;   // [16, 24): arrivals per rank band
-constexpr int kCtrRowBand = 64;    // [64, 64 + bands): arrivals per row band
-constexpr int kMaxRowBands = kCounterSlots - kCtrRowBand;
+constexpr int kCtrBand = 64;       // [64, 64 + bands): arrivals per band (rank bands first)
+constexpr int kMaxSlots = 1024;    // bound on resident decode workgroups used for sizing
 
 struct Shape {
   int K, N, r, g, T;
@@ -37,16 +35,18 @@ struct ProjPlan {
   int splits;  // K splits
 };
 
-// Work split of the fused decode kernel.
+// Work split of the fused decode kernel (stream-K over band x block units).
 struct DecodePlan {
   int bands;       // 64-row output bands
-  int splits;      // K splits across workgroups
   int rank_bands;  // 16-row bands of A
-  int workgroups() const { return (bands + rank_bands) * splits; }
+  int units;       // (bands + rank_bands) * K/128
+  int workgroups;  // persistent workgroups, each an equal run of units
+  int maxseg;      // bound on the workgroups sharing one band
 };
 
 ProjPlan plan_projection(const Shape& s);
-DecodePlan plan_decode(const Shape& s);
+// slots: workgroups the device keeps resident (2 per CU); sizing uses kMaxSlots.
+DecodePlan plan_decode(const Shape& s, int slots);
 
 // Byte offsets of the workspace regions for one call.
 struct Workspace {
