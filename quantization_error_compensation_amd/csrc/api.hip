@@ -31,19 +31,25 @@ DecodePlan plan_decode(const Shape& s, int slots) {
   DecodePlan pl;
   const int KB = s.KB();
   pl.bands = (s.N + kDecodeBandRows - 1) / kDecodeBandRows;
-  pl.rank_bands = s.r / 16;
+  pl.rank_bands = (s.r + 63) / 64;
   pl.units = (pl.bands + pl.rank_bands) * KB;
-  // At least 12 units (3 blocks per wave) per workgroup so the fixed latency of
-  // a workgroup is amortized; at most 128 units (32 blocks per wave, the size
-  // of the per-wave scale staging area).
+  // A rank unit moves (ranks in the band) x 256 B of A against 4 KB of codes
+  // for a row unit; it is costed 1.25 times that so the rank bands, which
+  // every row finisher waits for, complete early.
+  const int ranks = std::min(std::max(s.r, 1), 64);
+  pl.rank_cost = std::max(1, (5 * ranks + 63) / 64);
+  pl.cost = (long long)pl.rank_bands * KB * pl.rank_cost + (long long)pl.bands * KB;
+  // At least 8 cost units (one burst of row blocks) per workgroup.
   auto wgs = [&](int sl) {
-    int P = std::min(sl, (pl.units + 11) / 12);
-    P = std::max(P, (pl.units + 127) / 128);
-    return std::max(1, std::min(P, pl.units));
+    long long P = std::min<long long>(sl, std::max<long long>(1, pl.cost / 8));
+    return (int)std::max<long long>(1, std::min<long long>(P, pl.units));
   };
   pl.workgroups = wgs(std::min(std::max(slots, 1), kMaxSlots));
-  const int pmax = wgs(kMaxSlots);  // the partial-sum stride is sized for the bound
-  pl.maxseg = (KB + pl.units / pmax - 1) / (pl.units / pmax) + 1;
+  // A band of cost Cb meets at most ceil(Cb * P / cost) + 1 workgroup runs;
+  // the bound grows with P, so the workspace is sized for the largest P.
+  const long long pmax = wgs(kMaxSlots);
+  const long long cb = (long long)KB * std::max(pl.rank_cost, 1);
+  pl.maxseg = (int)std::min<long long>(pmax, (cb * pmax + pl.cost - 1) / pl.cost + 1);
   return pl;
 }
 

@@ -91,26 +91,20 @@ __device__ __forceinline__ float sigmoidf_safe(float z) {
   return e / (1.f + e);
 }
 
-// Cross-workgroup data without cache-wide fences.  A release fence writes the
-// whole XCD L2 back and an acquire invalidates it; done by every workgroup they
-// stall the streaming ones.  Data that one workgroup hands to another is
-// instead stored and loaded at device scope (sc1: coherent across XCDs, no
-// L2-wide maintenance), and the writer waits for its stores to complete
-// before it bumps the arrival counter.
-__device__ __forceinline__ void store_dev(float* p, float v) {
-  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ float load_dev(const float* p) {
-  return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
+// Counters shared between workgroups: relaxed atomics at device scope.
 __device__ __forceinline__ int load_dev(const int* p) {
   return __hip_atomic_load(const_cast<int*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 __device__ __forceinline__ void store_dev(int* p, int v) {
   __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
-// Wait until every memory operation this wave issued has completed.
-__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0); }
+// Wait until every memory operation this wave issued has completed.  The
+// compiler fences keep earlier stores from being moved past the wait.
+__device__ __forceinline__ void wait_vmem() {
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_waitcnt(0);
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
 
 // Raw buffer resource over [base, base + bytes): loads at offsets past the end
 // return zero, which masks rows past d_out and tokens past T.  Offsets are
@@ -128,6 +122,44 @@ __device__ __forceinline__ uint32_t bload4(rsrc_t r, uint32_t voff, uint32_t sof
 }
 __device__ __forceinline__ uint32_t bload2(rsrc_t r, uint32_t voff, uint32_t soff) {
   return (uint32_t)(uint16_t)__builtin_amdgcn_raw_buffer_load_b16(r, voff, soff, 0);
+}
+
+// Index of the calling wave in its workgroup as a wave-uniform value, so that
+// offsets derived from it stay in scalar registers (a buffer load whose scalar
+// offset the compiler cannot prove uniform is wrapped in a per-lane loop).
+__device__ __forceinline__ int wave_id() {
+  return __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+}
+
+// Data handed from one workgroup to another without cache-wide fences.  A
+// release fence writes the whole XCD L2 back and an acquire invalidates it;
+// done by every workgroup they stall the streaming ones.  Instead such data is
+// stored and loaded with the device-scope cache policy (sc1: coherent across
+// XCDs, no L2-wide maintenance), and the writer waits for its stores to
+// complete (wait_vmem) before it bumps the arrival counter.  These are plain
+// memory operations to the compiler, so many can be in flight at once; a
+// relaxed atomic of the same scope compiles to the same instruction but is
+// never reordered with other atomics, which serializes a run of them on the
+// memory latency.
+constexpr int kDeviceScope = 16;  // buffer cache-policy bits: sc1
+__device__ __forceinline__ float bload_dev(rsrc_t r, uint32_t voff, uint32_t soff) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, kDeviceScope));
+}
+__device__ __forceinline__ void bstore_dev(rsrc_t r, uint32_t voff, uint32_t soff, float v) {
+  __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), r, voff, soff, kDeviceScope);
+}
+
+// Plain global loads from a wave-uniform base plus a 32-bit byte offset (the
+// scalar-base addressing form: no per-load 64-bit address arithmetic and no
+// buffer descriptor held in scalar registers).
+__device__ __forceinline__ u32x4 gload16(const void* base, uint32_t off) {
+  return *reinterpret_cast<const u32x4*>(static_cast<const char*>(base) + off);
+}
+__device__ __forceinline__ uint32_t gload4(const void* base, uint32_t off) {
+  return *reinterpret_cast<const uint32_t*>(static_cast<const char*>(base) + off);
+}
+__device__ __forceinline__ uint32_t gload2(const void* base, uint32_t off) {
+  return *reinterpret_cast<const uint16_t*>(static_cast<const char*>(base) + off);
 }
 
 __device__ __forceinline__ u32x4 load16(const void* p) {

@@ -38,9 +38,11 @@ struct ProjPlan {
 // Work split of the fused decode kernel (stream-K over band x block units).
 struct DecodePlan {
   int bands;       // 64-row output bands
-  int rank_bands;  // 16-row bands of A
+  int rank_bands;  // 64-rank bands of A
   int units;       // (bands + rank_bands) * K/128
-  int workgroups;  // persistent workgroups, each an equal run of units
+  int rank_cost;   // cost of one rank unit (a row unit costs 1)
+  long long cost;  // total cost of all units
+  int workgroups;  // persistent workgroups, each a run of units of equal cost
   int maxseg;      // bound on the workgroups sharing one band
 };
 

@@ -6,23 +6,27 @@
 // streams the packed weights once, computes the rank-r projection of every
 // token once, gates it, and adds alpha * B * v before the single bf16 store.
 //
-// Work: a "unit" is one 128-column block of one band, where a band is either
-// 64 output rows of packed codes or 16 rows of A (bf16), both 4 KB per unit.
-// The rank bands come first in the unit order.  The P workgroups each take an
-// equal contiguous run of units (stream-K), processed band segment by band
-// segment; the four waves split a segment's blocks.  A band covered by
-// several workgroups has its partial sums combined by whichever arrives last
-// (in segment order, so results are deterministic); partial sums move through
+// Work.  A "band" is either 64 output rows of packed codes or 64 rows (ranks)
+// of A; a "unit" is one 128-column block of one band.  Rank bands come first
+// in the unit order.  A unit of a rank band moves 16 KB of bf16, a row unit
+// 4 KB of codes, so units carry a cost and the P persistent workgroups each
+// take a contiguous run of units of equal cost (stream-K).  A workgroup walks
+// its run band segment by band segment.  A band covered by several
+// workgroups has its partial sums combined by whichever arrives last (in
+// segment order, so results are deterministic); partial sums move through
 // device-scope stores and loads (coherent across XCDs, no L2-wide fence).
 //
-// Inner loop (per wave, per block, row band):
-//   * codes: 16 bytes per lane per 16-row tile (4 tiles), straight into
-//     registers, NS blocks ahead; bf16 operands 128 + c by byte permutes;
-//   * x: loaded with fully used cache lines (4 tokens x 256 B per load), put
-//     through the wave's own LDS slot and read back in the matrix-core layout
-//     (a direct fragment load would touch two half-used lines per token);
-//   * group scales and zero-points: staged in LDS per segment, not reloaded
-//     per block;
+// Inside a segment the four waves of a workgroup own one 16-row tile each
+// and walk the same K blocks in bursts of NS blocks:
+//   * x of the burst is loaded once per workgroup (each wave 4 tokens x
+//     256 B per instruction, full cache lines), permuted into the
+//     matrix-core K order and written to a double-buffered LDS area; one
+//     barrier per burst publishes it to all four waves;
+//   * codes: 16 bytes per lane per block (16 rows x 64 B per instruction),
+//     all NS blocks issued back to back; bf16 operands 128 + c by byte
+//     permutes;
+//   * group scales and zero-points: staged per 32-block chunk in each wave's
+//     LDS area with loads that cover whole runs of a row's metadata;
 //   * matrix cores 16x16x32: tokens (padded to 16 or 32) x 16 rows x 32 K; a
 //     ones-operand product gives the block sums of x that remove the offset.
 // The band finisher adds alpha * B * v as a small K = r matrix-core product
@@ -30,8 +34,9 @@
 //
 // Waiting: finishers of row bands wait for the rank bands to publish.  Rank
 // units are the first units, owned by the lowest workgroup indices, which the
-// dispatcher starts first, so they run before anyone waits; the wait is
-// bounded and raises an error word instead of hanging.
+// dispatcher starts first, so they run before anyone waits; rank units are
+// costed above their byte count so those workgroups finish early.  The wait
+// is bounded and raises an error word instead of hanging.
 #include "common.hpp"
 #include "internal.hpp"
 
@@ -53,266 +58,256 @@ struct DecodeParams {
   int* ctr;                // counter words
   uint16_t* y;             // [T][N] bf16
   int T, K, N, r, G, ZW, has_z;
-  int KB, RB, NB, U, P, maxseg;
+  int KB;                  // 128-column blocks per row
+  int RB;                  // rank bands (64 ranks each)
+  int NB;                  // row bands (64 rows each)
+  int P;                   // workgroups
+  int rank_cost;           // cost of a rank unit; a row unit costs 1
+  long long ctot;          // total cost of all units
+  int maxseg;              // bound on the workgroups sharing one band
 };
 
-constexpr int RT = 4;                  // 16-row tiles per row band (64 rows)
-constexpr int XROW = 272;              // LDS row of one token: 256 B + 16 B pad
-constexpr int kMetaBlocks = 32;        // max blocks of one wave in one segment
-constexpr int kMetaBytes = 64 * kMetaBlocks * 4;
-constexpr int kSpinLimit = 1 << 20;    // bounded wait (about a second)
+constexpr int XROW = 272;            // LDS row of one token: 256 B + 16 B pad
+constexpr int kSpinLimit = 1 << 20;  // bounded wait (about a second)
 
+// Blocks per burst: 8 (row bands) / 4 (rank bands) up to 16 tokens, half that
+// up to 32 tokens, so one LDS buffer of x always holds 128 token-blocks.
 template <int MT>
-struct Lds {
-  static constexpr int kXBytes = MT * 16 * XROW;
-  static constexpr int kWave = kXBytes + kMetaBytes;
-  static constexpr int kTotal = 4 * kWave;
+struct Burst {
+  static constexpr int kRow = MT == 1 ? 8 : 4;
+  static constexpr int kRank = kRow / 2;
+  static constexpr int kBuf = kRow * 16 * MT * XROW;  // bytes of one x buffer
 };
 
-__device__ __forceinline__ int owner_of(long long u, const DecodeParams& p) {
-  return (int)(((u + 1) * p.P - 1) / p.U);
+// ------------------------------------------------------------- partition
+// Cost of the first u units, and the first unit of workgroup w: the smallest
+// u with S(u) * P >= w * ctot.  owner_of(u) is the workgroup whose run holds
+// unit u.
+__device__ __forceinline__ long long cost_prefix(const DecodeParams& p, long long u) {
+  const long long ru = (long long)p.RB * p.KB;
+  return u <= ru ? u * p.rank_cost : ru * p.rank_cost + (u - ru);
+}
+__device__ __forceinline__ long long unit_begin(const DecodeParams& p, int w) {
+  const long long X = (long long)w * p.ctot;
+  const long long ru = (long long)p.RB * p.KB;
+  const long long rc = (long long)p.rank_cost * p.P;
+  if (X <= ru * rc) return (X + rc - 1) / rc;
+  return ru + (X - ru * rc + p.P - 1) / p.P;
+}
+__device__ __forceinline__ int owner_of(const DecodeParams& p, long long u) {
+  return (int)(cost_prefix(p, u) * p.P / p.ctot);
 }
 
-// The blocks of `wave` inside a segment [lo, hi).
-__device__ __forceinline__ void wave_range(int lo, int hi, int wave, int& b0, int& b1) {
-  const int nb = hi - lo;
-  b0 = lo + nb * wave / 4;
-  b1 = lo + nb * (wave + 1) / 4;
-}
+// ------------------------------------------------------------- x staging
+// x of blocks [b, b + NS) into an LDS buffer [NS][16*MT tokens][XROW], each
+// 16-byte piece already in the matrix-core K order.  Wave w loads tokens
+// 4w + 16m .. +3 (lane: token 4w + 16m + l/16, piece l%16); a wave whose
+// tokens all lie past T skips its loads and writes zeros.
+template <int MT, int NS>
+struct XStage {
+  u32x4 g[NS][MT];
+};
 
-// Runs compute(b, stage) for b in [b0, b1) with the loads of the next NS-1
-// blocks in flight.  issue() runs for every slot with the block clamped into
-// range, so the count of loads in flight never depends on a branch.
-template <int NS, class Stage, class Issue, class Compute>
-__device__ __forceinline__ void stream(int b0, int b1, Stage (&st)[NS], Issue issue,
-                                       Compute compute) {
-  if (b0 >= b1) return;
-  const int last = b1 - 1;
-#pragma unroll
-  for (int i = 0; i < NS - 1; ++i) issue(min(b0 + i, last), st[i]);
-  for (int base = b0; base < b1; base += NS) {
-#pragma unroll
-    for (int i = 0; i < NS; ++i) {
-      issue(min(base + i + NS - 1, last), st[(i + NS - 1) % NS]);
-      if (base + i < b1) compute(base + i, st[i]);
+template <int MT, int NS>
+__device__ __forceinline__ void x_issue(const DecodeParams& p, int wave, int lane, int b, int hi,
+                                        XStage<MT, NS>& s) {
+  const uint32_t xrowB = (uint32_t)p.K * 2;
+  for (int m = 0; m < MT; ++m) {
+    const int t0 = 4 * wave + 16 * m;
+    // tokens past T load token T - 1: their products land in output rows
+    // that are never stored
+    const uint32_t vo = (uint32_t)min(t0 + (lane >> 4), p.T - 1) * xrowB + 16u * (lane & 15);
+    if (t0 < p.T) {
+      for (int i = 0; i < NS; ++i) s.g[i][m] = gload16(p.x, vo + (uint32_t)min(b + i, hi - 1) * 256);
+    } else {
+      for (int i = 0; i < NS; ++i) s.g[i][m] = u32x4{0u, 0u, 0u, 0u};
     }
   }
 }
 
-// x of one block: MT*16 tokens x 256 bytes, loaded as 4 tokens x 256 B per
-// instruction (lane l: token 4c + l/16, 16-byte piece l%16); tokens past T
-// read as zero through the buffer bound.
-template <int MT>
-struct XLoad {
-  u32x4 g[4 * MT];
-};
-
-template <int MT>
-__device__ __forceinline__ void x_issue(rsrc_t xs, uint32_t xrowB, int lane, int blk,
-                                        XLoad<MT>& s) {
-  const uint32_t base = (uint32_t)(lane >> 4) * xrowB + 16u * (lane & 15);
-  for (int c = 0; c < 4 * MT; ++c)
-    s.g[c] = bload16(xs, base + 4u * c * xrowB, (uint32_t)blk * 256);
+template <int MT, int NS>
+__device__ __forceinline__ void x_store(uint8_t* buf, int wave, int lane,
+                                        const XStage<MT, NS>& s) {
+  for (int i = 0; i < NS; ++i)
+    for (int m = 0; m < MT; ++m) {
+      const int t = 4 * wave + 16 * m + (lane >> 4);
+      *reinterpret_cast<u32x4*>(buf + (i * 16 * MT + t) * XROW + 16 * (lane & 15)) =
+          x_permute8(s.g[i][m]);
+    }
 }
 
-// Write the block to this wave's LDS slot, read back fragment (mt, i) of lane
-// (token c16 + 16 mt, K group q).  The packed-code path needs piece 4q + i
-// (a lane's 16 code bytes span 32 consecutive columns); the rank path, where
-// both operands are plain bf16, uses piece 4i + q so that one A load reads 64
-// consecutive bytes of each row.
-template <int MT, bool RANK_ORDER>
-__device__ __forceinline__ void x_to_frags(uint8_t* slot, int lane, const XLoad<MT>& s,
-                                           u32x4 (&f)[MT][4]) {
-  const int tt = lane >> 4, pc = lane & 15;
-  for (int c = 0; c < 4 * MT; ++c)
-    *reinterpret_cast<u32x4*>(slot + (4 * c + tt) * XROW + 16 * pc) = s.g[c];
+// Fragment (mt, j) of block i for lane (token c16 + 16 mt, K group q): piece
+// 4q + j of the token's 256-byte block row (columns 32q + 8j .. +7).
+template <int MT>
+__device__ __forceinline__ void x_frags(const uint8_t* buf, int i, int lane, u32x4 (&f)[MT][4]) {
   const int q = lane >> 4, c16 = lane & 15;
   for (int mt = 0; mt < MT; ++mt)
-    for (int i = 0; i < 4; ++i) {
-      const int piece = RANK_ORDER ? 4 * i + q : 4 * q + i;
-      f[mt][i] = *reinterpret_cast<const u32x4*>(slot + (16 * mt + c16) * XROW + piece * 16);
-    }
+    for (int j = 0; j < 4; ++j)
+      f[mt][j] = *reinterpret_cast<const u32x4*>(buf + (i * 16 * MT + 16 * mt + c16) * XROW +
+                                                 (4 * q + j) * 16);
 }
 
-// ------------------------------------------------------------- rank segment
-// 16 rows of A (ranks 16 rb .. 16 rb + 15), blocks [lo, hi).  Every wave
-// returns the workgroup sum of u in uo.
+// ------------------------------------------------------------ rank segment
+// Ranks 64 rb + 16 wave + c16, blocks [lo, hi): u = x A^T over the segment.
 template <int MT>
-__device__ void rank_segment(const DecodeParams& p, int rb, int lo, int hi, uint8_t* pool,
-                             f32x4 (&uo)[MT]) {
-  constexpr int NS = 3;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, q = lane >> 4, c16 = lane & 15;
-  uint8_t* slot = pool + wave * Lds<MT>::kWave;
-  int b0, b1;
-  wave_range(lo, hi, wave, b0, b1);
-  const uint32_t xrowB = (uint32_t)p.K * 2;
-  const rsrc_t xs = make_rsrc(p.x, (uint32_t)p.T * xrowB);
-  const rsrc_t as = make_rsrc(p.A + (size_t)16 * rb * p.K, 16 * xrowB);
-  const uint32_t ao = (uint32_t)c16 * xrowB + 16 * q;  // piece 4i + q of row c16
+__device__ void rank_segment(const DecodeParams& p, int rb, int lo, int hi, uint8_t* xlds,
+                             int& burst, f32x4 (&uo)[MT]) {
+  constexpr int NS = Burst<MT>::kRank;
+  const int lane = threadIdx.x & 63, wave = wave_id(), q = lane >> 4, c16 = lane & 15;
+  // A tile of ranks j0 .. j0 + 15; a wave past r reads the last tile again
+  // (its u columns are never published)
+  const int j0 = min(64 * rb + 16 * wave, p.r - 16);
+  const uint32_t arowB = (uint32_t)p.K * 2;
+  const uint16_t* At = p.A + (size_t)j0 * p.K;
+  const uint32_t ao = (uint32_t)c16 * arowB + 64u * q;  // pieces 4q .. 4q + 3 of row c16
+  for (int mt = 0; mt < MT; ++mt) uo[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  struct Stage {
-    u32x4 a[4];
-    XLoad<MT> x;
-  };
-  Stage st[NS];
-  f32x4 u[MT];
-  for (int mt = 0; mt < MT; ++mt) u[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
-  stream<NS>(
-      b0, b1, st,
-      [&](int blk, Stage& s) {
-        for (int i = 0; i < 4; ++i) s.a[i] = bload16(as, ao + 64 * i, (uint32_t)blk * 256);
-        x_issue<MT>(xs, xrowB, lane, blk, s.x);
-      },
-      [&](int, const Stage& s) {
+  for (int b = lo; b < hi; b += NS, ++burst) {
+    uint8_t* buf = xlds + (burst & 1) * Burst<MT>::kBuf;
+    XStage<MT, NS> xsg;
+    x_issue<MT, NS>(p, wave, lane, b, hi, xsg);
+    u32x4 a[NS][4];
+    for (int i = 0; i < NS; ++i)
+      for (int j = 0; j < 4; ++j)
+        a[i][j] = gload16(At, ao + 16 * j + (uint32_t)min(b + i, hi - 1) * 256);
+    x_store<MT, NS>(buf, wave, lane, xsg);
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < NS; ++i) {
+      if (b + i < hi) {
         u32x4 xf[MT][4];
-        x_to_frags<MT, true>(slot, lane, s.x, xf);
-        for (int mt = 0; mt < MT; ++mt)
-          for (int i = 0; i < 4; ++i) u[mt] = mfma16x16x32(xf[mt][i], s.a[i], u[mt]);
-      });
-
-  __syncthreads();
-  float* red = reinterpret_cast<float*>(pool);  // [4][MT][4][64]
-  for (int mt = 0; mt < MT; ++mt)
-    for (int v = 0; v < 4; ++v) red[((wave * MT + mt) * 4 + v) * 64 + lane] = u[mt][v];
-  __syncthreads();
-  for (int mt = 0; mt < MT; ++mt)
-    for (int v = 0; v < 4; ++v) {
-      float s = 0.f;
-      for (int w = 0; w < 4; ++w) s += red[((w * MT + mt) * 4 + v) * 64 + lane];
-      uo[mt][v] = s;
+        x_frags<MT>(buf, i, lane, xf);
+        for (int j = 0; j < 4; ++j) {
+          const u32x4 ap = x_permute8(a[i][j]);
+          for (int mt = 0; mt < MT; ++mt) uo[mt] = mfma16x16x32(xf[mt][j], ap, uo[mt]);
+        }
+      }
     }
+  }
 }
 
 // -------------------------------------------------------------- row segment
-// 64 output rows n0 .. n0 + 63, blocks [lo, hi).  Returns the partial y of
-// row tile `wave` in yo (scales already applied).
-template <int MT, bool GROUPED>
-__device__ void row_segment(const DecodeParams& p, int band, int lo, int hi, uint8_t* pool,
-                            f32x4 (&yo)[MT]) {
-  constexpr int NS = MT == 1 ? 3 : 2;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, q = lane >> 4, c16 = lane & 15;
-  uint8_t* slot = pool + wave * Lds<MT>::kWave;
-  uint32_t* meta = reinterpret_cast<uint32_t*>(slot + Lds<MT>::kXBytes);  // [64 rows][32 blocks]
-  const int n0 = band * kDecodeBandRows;
-  const int rows = min(kDecodeBandRows, p.N - n0);
-  int b0, b1;
-  wave_range(lo, hi, wave, b0, b1);
-  const int nwb = b1 - b0;
+// Group scales and zero-points of a wave's 16 rows are staged per chunk of
+// kMetaChunk blocks in the wave's own LDS area: ms[16][kMetaChunk] fp16 bits
+// and mz[16][8] zero-point words (word w0 + k holds blocks 8(w0 + k) ..).
+// Each staging load covers 2 rows x 32 consecutive scales (or 16 rows x 4
+// words), so a row's metadata costs a few cache-line requests per chunk
+// rather than one per burst.
+constexpr int kMetaChunk = 32;
+constexpr int kMetaWave = 16 * kMetaChunk * 2 + 16 * 8 * 4;  // bytes per wave
 
-  if constexpr (GROUPED) {
-    // scale (fp16 bits) and zero-point of (row, block) for this wave's blocks
-    for (int e = lane; e < 64 * nwb; e += 64) {
-      const int row = e / nwb, bb = e - row * nwb, blk = b0 + bb;
-      const int n = n0 + min(row, rows - 1);
-      const uint32_t s = p.scales[(size_t)n * p.G + blk];
-      const uint32_t z =
-          p.has_z ? (p.zeros[(size_t)n * p.ZW + (blk >> 3)] >> (4 * (blk & 7))) & 15u : 8u;
-      meta[row * kMetaBlocks + bb] = s | (z << 16);
+// Rows 64 band + 16 wave + c16 (this wave's tile), blocks [lo, hi): partial
+// y with the scales applied.
+template <int MT, bool GROUPED>
+__device__ void row_segment(const DecodeParams& p, int band, int lo, int hi, uint8_t* xlds,
+                            uint8_t* mlds, int& burst, f32x4 (&yo)[MT]) {
+  constexpr int NS = Burst<MT>::kRow;
+  const int lane = threadIdx.x & 63, wave = wave_id(), q = lane >> 4, c16 = lane & 15;
+  // Tile of rows rc .. rc + 15; a tile past N (last band of an N that is not
+  // a multiple of 64) reads the last tile again and stores nothing.
+  const int rc = min(band * 64 + 16 * wave, p.N - 16);
+  const uint32_t wrowB = (uint32_t)p.K / 2;
+  const uint32_t* Wt = p.wq + (size_t)rc * (p.K / 8);
+  const uint32_t wo = (uint32_t)c16 * wrowB + 16u * q;
+  const uint16_t* St = p.scales + (size_t)rc * p.G;
+  const uint32_t* Zt = p.zeros + (size_t)rc * p.ZW;
+  const u32x4 ones = {kBf16One, kBf16One, kBf16One, kBf16One};
+  uint16_t* ms = reinterpret_cast<uint16_t*>(mlds + wave * kMetaWave);
+  uint32_t* mz = reinterpret_cast<uint32_t*>(mlds + wave * kMetaWave + 16 * kMetaChunk * 2);
+  int c0 = lo, w0 = lo >> 3;  // first block and first zero-point word of the staged chunk
+
+  f32x4 acc[MT], ssum[MT];
+  for (int mt = 0; mt < MT; ++mt) acc[mt] = ssum[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  for (int b = lo; b < hi; b += NS, ++burst) {
+    uint8_t* buf = xlds + (burst & 1) * Burst<MT>::kBuf;
+    uint32_t sv[8], zv[2];
+    const bool stage = GROUPED && (b - lo) % kMetaChunk == 0;
+    if (stage) {
+      c0 = b;
+      w0 = b >> 3;
+      const int c1 = min(b + kMetaChunk, hi);
+      const int blk = min(c0 + (lane & 31), c1 - 1);
+      for (int k = 0; k < 8; ++k)
+        sv[k] = gload2(St, (uint32_t)((2 * k + (lane >> 5)) * p.G + blk) * 2);
+      for (int e = 0; e < 2; ++e) {
+        const int wd = min(w0 + (lane & 3) + 4 * e, (c1 - 1) >> 3);
+        zv[e] = p.has_z ? gload4(Zt, (uint32_t)((lane >> 2) * p.ZW + wd) * 4) : 0x88888888u;
+      }
+    }
+    XStage<MT, NS> xsg;
+    x_issue<MT, NS>(p, wave, lane, b, hi, xsg);
+    u32x4 w[NS];
+    for (int i = 0; i < NS; ++i) w[i] = gload16(Wt, wo + (uint32_t)min(b + i, hi - 1) * 64);
+    if (stage) {
+      for (int k = 0; k < 8; ++k) ms[(2 * k + (lane >> 5)) * kMetaChunk + (lane & 31)] = (uint16_t)sv[k];
+      for (int e = 0; e < 2; ++e) mz[(lane >> 2) * 8 + (lane & 3) + 4 * e] = zv[e];
+    }
+    x_store<MT, NS>(buf, wave, lane, xsg);
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < NS; ++i) {
+      if (b + i >= hi) continue;
+      u32x4 xf[MT][4];
+      x_frags<MT>(buf, i, lane, xf);
+      u32x4 wb[4];
+      wb[0] = codes_to_bf16_offset(w[i].x);
+      wb[1] = codes_to_bf16_offset(w[i].y);
+      wb[2] = codes_to_bf16_offset(w[i].z);
+      wb[3] = codes_to_bf16_offset(w[i].w);
+      if constexpr (GROUPED) {
+        const int blk = b + i;
+        const float sc = half_bits_to_f32(ms[c16 * kMetaChunk + (blk - c0)]);
+        const uint32_t z = (mz[c16 * 8 + ((blk >> 3) - w0)] >> (4 * (blk & 7))) & 15u;
+        const float nz = -(float)(128u + z);
+        for (int mt = 0; mt < MT; ++mt) {
+          f32x4 sb = mfma16x16x32(xf[mt][0], ones, f32x4{0.f, 0.f, 0.f, 0.f});
+          f32x4 P = mfma16x16x32(xf[mt][0], wb[0], f32x4{0.f, 0.f, 0.f, 0.f});
+          for (int j = 1; j < 4; ++j) {
+            sb = mfma16x16x32(xf[mt][j], ones, sb);
+            P = mfma16x16x32(xf[mt][j], wb[j], P);
+          }
+          for (int v = 0; v < 4; ++v) acc[mt][v] = fmaf(sc, fmaf(nz, sb[v], P[v]), acc[mt][v]);
+        }
+      } else {
+        for (int mt = 0; mt < MT; ++mt)
+          for (int j = 0; j < 4; ++j) {
+            ssum[mt] = mfma16x16x32(xf[mt][j], ones, ssum[mt]);
+            acc[mt] = mfma16x16x32(xf[mt][j], wb[j], acc[mt]);
+          }
+      }
     }
   }
-
-  const uint32_t wrowB = (uint32_t)p.K / 2, xrowB = (uint32_t)p.K * 2;
-  const rsrc_t ws = make_rsrc(p.wq + (size_t)n0 * (p.K / 8), (uint32_t)rows * wrowB);
-  const rsrc_t xs = make_rsrc(p.x, (uint32_t)p.T * xrowB);
-  uint32_t wo[RT];
-  for (int rt = 0; rt < RT; ++rt) wo[rt] = (uint32_t)(16 * rt + c16) * wrowB + 16 * q;
-
-  struct Stage {
-    u32x4 w[RT];
-    XLoad<MT> x;
-  };
-  Stage st[NS];
-  f32x4 acc[MT][RT], ssum[MT];
-  for (int mt = 0; mt < MT; ++mt) {
-    ssum[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
-    for (int rt = 0; rt < RT; ++rt) acc[mt][rt] = f32x4{0.f, 0.f, 0.f, 0.f};
-  }
-  const u32x4 ones = {kBf16One, kBf16One, kBf16One, kBf16One};
-
-  stream<NS>(
-      b0, b1, st,
-      [&](int blk, Stage& s) {
-        for (int rt = 0; rt < RT; ++rt) s.w[rt] = bload16(ws, wo[rt], (uint32_t)blk * 64);
-        x_issue<MT>(xs, xrowB, lane, blk, s.x);
-      },
-      [&](int blk, const Stage& s) {
-        u32x4 xp[MT][4];
-        x_to_frags<MT, false>(slot, lane, s.x, xp);
-        for (int mt = 0; mt < MT; ++mt)
-          for (int i = 0; i < 4; ++i) xp[mt][i] = x_permute8(xp[mt][i]);
-        f32x4 sb[MT];
-        for (int mt = 0; mt < MT; ++mt) {
-          if constexpr (GROUPED) {
-            sb[mt] = mfma16x16x32(xp[mt][0], ones, f32x4{0.f, 0.f, 0.f, 0.f});
-            for (int i = 1; i < 4; ++i) sb[mt] = mfma16x16x32(xp[mt][i], ones, sb[mt]);
-          } else {
-            for (int i = 0; i < 4; ++i) ssum[mt] = mfma16x16x32(xp[mt][i], ones, ssum[mt]);
-          }
-        }
-        for (int rt = 0; rt < RT; ++rt) {
-          u32x4 wb[4];
-          wb[0] = codes_to_bf16_offset(s.w[rt].x);
-          wb[1] = codes_to_bf16_offset(s.w[rt].y);
-          wb[2] = codes_to_bf16_offset(s.w[rt].z);
-          wb[3] = codes_to_bf16_offset(s.w[rt].w);
-          if constexpr (GROUPED) {
-            const uint32_t m = meta[(16 * rt + c16) * kMetaBlocks + (blk - b0)];
-            const float sc = half_bits_to_f32((uint16_t)(m & 0xFFFFu));
-            const float mz = -(float)(128u + (m >> 16));
-            for (int mt = 0; mt < MT; ++mt) {
-              f32x4 P = mfma16x16x32(xp[mt][0], wb[0], f32x4{0.f, 0.f, 0.f, 0.f});
-              P = mfma16x16x32(xp[mt][1], wb[1], P);
-              P = mfma16x16x32(xp[mt][2], wb[2], P);
-              P = mfma16x16x32(xp[mt][3], wb[3], P);
-              for (int v = 0; v < 4; ++v)
-                acc[mt][rt][v] = fmaf(sc, fmaf(mz, sb[mt][v], P[v]), acc[mt][rt][v]);
-            }
-          } else {
-            for (int mt = 0; mt < MT; ++mt)
-              for (int i = 0; i < 4; ++i) acc[mt][rt] = mfma16x16x32(xp[mt][i], wb[i], acc[mt][rt]);
-          }
-        }
-      });
 
   if constexpr (!GROUPED) {  // per-channel: one scale and one offset correction per row
-    for (int rt = 0; rt < RT; ++rt) {
-      const int n = n0 + min(16 * rt + c16, rows - 1);
-      const float sc = half_bits_to_f32(p.scales[n]);
-      const int z = p.has_z ? (int)(p.zeros[(size_t)n * p.ZW] & 15u) : 8;
-      const float mz = -(float)(128 + z);
-      for (int mt = 0; mt < MT; ++mt)
-        for (int v = 0; v < 4; ++v) acc[mt][rt][v] = sc * fmaf(mz, ssum[mt][v], acc[mt][rt][v]);
-    }
+    const int n = rc + c16;
+    const float sc = half_bits_to_f32(p.scales[n]);
+    const int z = p.has_z ? (int)(p.zeros[(size_t)n * p.ZW] & 15u) : 8;
+    const float mz = -(float)(128 + z);
+    for (int mt = 0; mt < MT; ++mt)
+      for (int v = 0; v < 4; ++v) acc[mt][v] = sc * fmaf(mz, ssum[mt][v], acc[mt][v]);
   }
-
-  // Sum the four waves; wave w then owns row tile w.
-  __syncthreads();
-  float* red = reinterpret_cast<float*>(pool);  // [4][MT][RT][4][64]
-  for (int mt = 0; mt < MT; ++mt)
-    for (int rt = 0; rt < RT; ++rt)
-      for (int v = 0; v < 4; ++v)
-        red[(((wave * MT + mt) * RT + rt) * 4 + v) * 64 + lane] = acc[mt][rt][v];
-  __syncthreads();
-  for (int mt = 0; mt < MT; ++mt)
-    for (int v = 0; v < 4; ++v) {
-      float s = 0.f;
-      for (int w = 0; w < 4; ++w) s += red[(((w * MT + mt) * RT + wave) * 4 + v) * 64 + lane];
-      yo[mt][v] = s;
-    }
+  for (int mt = 0; mt < MT; ++mt) yo[mt] = acc[mt];
 }
 
-// Partial sums of a band: [maxseg][T][64] floats per band, written and read
-// at device scope.  Column c of a partial is row c of a row band, or rank
-// 16 rb + c of a rank band (only columns 0..15 used).
+// ------------------------------------------------------------ partial sums
+// [maxseg][T][64] floats per band, written and read at device scope.  Column
+// c of a partial is row 64 band + c of a row band, or rank 64 rb + c.
+__device__ __forceinline__ rsrc_t part_rsrc(const DecodeParams& p, int band) {
+  const uint32_t bytes = (uint32_t)p.maxseg * p.T * 64 * 4;
+  return make_rsrc(p.part + (size_t)band * p.maxseg * p.T * 64, bytes);
+}
+
 template <int MT>
 __device__ __forceinline__ void put_part(const DecodeParams& p, int band, int sidx, int col,
                                          const f32x4 (&v)[MT]) {
   const int q = (threadIdx.x & 63) >> 4;
-  float* base = p.part + ((size_t)band * p.maxseg + sidx) * p.T * 64;
+  const rsrc_t r = part_rsrc(p, band);
+  const uint32_t so = (uint32_t)sidx * p.T * 256;
   for (int mt = 0; mt < MT; ++mt)
     for (int i = 0; i < 4; ++i) {
       const int t = 16 * mt + 4 * q + i;
-      if (t < p.T) store_dev(base + (size_t)t * 64 + col, v[mt][i]);
+      if (t < p.T) bstore_dev(r, so + (uint32_t)(t * 64 + col) * 4, 0, v[mt][i]);
     }
 }
 
@@ -320,39 +315,54 @@ template <int MT>
 __device__ __forceinline__ void sum_parts(const DecodeParams& p, int band, int nseg, int col,
                                           f32x4 (&v)[MT]) {
   const int q = (threadIdx.x & 63) >> 4;
+  const rsrc_t r = part_rsrc(p, band);
+  uint32_t off[MT][4];
   for (int mt = 0; mt < MT; ++mt)
     for (int i = 0; i < 4; ++i) {
       const int t = min(16 * mt + 4 * q + i, p.T - 1);
-      float s = 0.f;
-#pragma unroll 4
-      for (int k = 0; k < nseg; ++k)
-        s += load_dev(p.part + (((size_t)band * p.maxseg + k) * p.T + t) * 64 + col);
-      v[mt][i] = s;
+      off[mt][i] = (uint32_t)(t * 64 + col) * 4;
+      v[mt][i] = 0.f;
     }
+  // Loads of 8 partials in flight at a time; summed in segment order.
+  const uint32_t seg = (uint32_t)p.T * 256;
+  for (int k0 = 0; k0 < nseg; k0 += 8) {
+    float t[8][MT][4];
+    for (int kk = 0; kk < 8; ++kk) {
+      const uint32_t so = (uint32_t)min(k0 + kk, nseg - 1) * seg;
+      for (int mt = 0; mt < MT; ++mt)
+        for (int i = 0; i < 4; ++i) t[kk][mt][i] = bload_dev(r, off[mt][i], so);
+    }
+    for (int kk = 0; kk < 8; ++kk)
+      if (k0 + kk < nseg)
+        for (int mt = 0; mt < MT; ++mt)
+          for (int i = 0; i < 4; ++i) v[mt][i] += t[kk][mt][i];
+  }
 }
 
-// Finish a rank band: gate and publish alpha * v for ranks 16 rb .. +15.
+// Finish a rank band: gate and publish alpha * v for this wave's 16 ranks.
 template <int MT>
 __device__ void finish_rank(const DecodeParams& p, int rb, const f32x4 (&u)[MT]) {
-  const int lane = threadIdx.x & 63, q = lane >> 4, c16 = lane & 15;
-  const int j = 16 * rb + c16;
+  const int lane = threadIdx.x & 63, wave = wave_id(), q = lane >> 4, c16 = lane & 15;
+  const int j = 64 * rb + 16 * wave + c16;
+  if (j >= p.r) return;
   const float g = p.gv[j], b = p.bv[j];
+  const rsrc_t wr = make_rsrc(p.wv32, (uint32_t)p.T * p.r * 4);
   for (int mt = 0; mt < MT; ++mt)
     for (int i = 0; i < 4; ++i) {
       const int t = 16 * mt + 4 * q + i;
       if (t < p.T) {
         const float uu = u[mt][i];
-        store_dev(&p.wv32[(size_t)t * p.r + j], p.alpha * (sigmoidf_safe(fmaf(g, uu, b)) * uu));
+        bstore_dev(wr, (uint32_t)(t * p.r + j) * 4, 0,
+                   p.alpha * (sigmoidf_safe(fmaf(g, uu, b)) * uu));
       }
     }
 }
 
-// Finish a row band (wave = row tile): + alpha * v B^T, then store y.
+// Finish a row band (this wave's tile): + alpha * v B^T, then store y.
 template <int MT>
 __device__ void finish_row(const DecodeParams& p, int band, f32x4 (&yv)[MT]) {
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, q = lane >> 4, c16 = lane & 15;
-  const int n0 = band * kDecodeBandRows;
-  const int nrow = n0 + 16 * wave + c16;
+  const int tid = threadIdx.x, lane = tid & 63, wave = wave_id(), q = lane >> 4, c16 = lane & 15;
+  const int nrow = band * 64 + 16 * wave + c16;
   if (p.r > 0) {
     if (tid == 0) {
       int spins = 0;
@@ -366,6 +376,7 @@ __device__ void finish_row(const DecodeParams& p, int band, f32x4 (&yv)[MT]) {
     }
     __syncthreads();
     const rsrc_t bs = make_rsrc(p.B, (uint32_t)p.N * p.r * 2);
+    const rsrc_t wr = make_rsrc(p.wv32, (uint32_t)p.T * p.r * 4);
     const uint32_t bro = (uint32_t)min(nrow, p.N - 1) * p.r * 2;
     for (int j0 = 0; j0 < p.r; j0 += 32) {
       const int jj = j0 + 8 * q;  // this lane's 8 ranks of the K = 32 step
@@ -375,10 +386,12 @@ __device__ void finish_row(const DecodeParams& p, int band, f32x4 (&yv)[MT]) {
         const int t = min(16 * mt + c16, p.T - 1);
         u32x4 hi = {0, 0, 0, 0}, lo = {0, 0, 0, 0};
         if (jok) {
-          const float* src = p.wv32 + (size_t)t * p.r + jj;
+          const uint32_t src = (uint32_t)(t * p.r + jj) * 4;
+          float wv[8];
+          for (int e = 0; e < 8; ++e) wv[e] = bload_dev(wr, src + 4 * e, 0);
           uint32_t h[8], l[8];
           for (int e = 0; e < 8; ++e) {
-            const float v = load_dev(src + e);
+            const float v = wv[e];
             h[e] = f32_to_bf16_rne(v);
             l[e] = f32_to_bf16_rne(v - __uint_as_float(h[e] << 16));
           }
@@ -402,45 +415,50 @@ __device__ void finish_row(const DecodeParams& p, int band, f32x4 (&yv)[MT]) {
 
 template <int MT, bool GROUPED>
 __global__ __launch_bounds__(256, 2) void decode_kernel(DecodeParams p) {
-  __shared__ __attribute__((aligned(16))) uint8_t pool[Lds<MT>::kTotal];
+  __shared__ __attribute__((aligned(16))) uint8_t xlds[2 * Burst<MT>::kBuf];
+  __shared__ __attribute__((aligned(16))) uint8_t mlds[GROUPED ? 4 * kMetaWave : 16];
   __shared__ int s_last;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, c16 = lane & 15;
+  const int tid = threadIdx.x, lane = tid & 63, wave = wave_id(), c16 = lane & 15;
   const int wg = blockIdx.x;
-  const long long u0 = (long long)p.U * wg / p.P, u1 = (long long)p.U * (wg + 1) / p.P;
+  const long long u0 = unit_begin(p, wg), u1 = unit_begin(p, wg + 1);
+  int burst = 0;
 
   for (long long u = u0; u < u1;) {
     const int band = (int)(u / p.KB);
-    const long long bend = (long long)(band + 1) * p.KB;
-    const int lo = (int)(u - (long long)band * p.KB);
-    const int hi = (int)(min(u1, bend) - (long long)band * p.KB);
+    const long long bbeg = (long long)band * p.KB, bend = bbeg + p.KB;
+    const int lo = (int)(u - bbeg);
+    const int hi = (int)(min(u1, bend) - bbeg);
     u = min(u1, bend);
-    const int first = owner_of((long long)band * p.KB, p);
-    const int nseg = owner_of(bend - 1, p) - first + 1;
+    const int first = owner_of(p, bbeg);
+    const int nseg = owner_of(p, bend - 1) - first + 1;
     const int sidx = wg - first;
     const bool rank = band < p.RB;
+    if (nseg > p.maxseg) {  // cannot happen with a workspace sized by the planner
+      if (tid == 0) atomicOr(&p.ctr[kCtrError], 2);
+      continue;
+    }
 
     f32x4 v[MT];
-    if (rank) rank_segment<MT>(p, band, lo, hi, pool, v);
-    else row_segment<MT, GROUPED>(p, band - p.RB, lo, hi, pool, v);
-    const int col = rank ? c16 : 16 * wave + c16;
-    const bool owner = rank ? wave == 0 : true;  // rank band: one copy of the sum
+    if (rank) rank_segment<MT>(p, band, lo, hi, xlds, burst, v);
+    else row_segment<MT, GROUPED>(p, band - p.RB, lo, hi, xlds, mlds, burst, v);
+    const int col = 16 * wave + c16;
 
     bool fin = nseg == 1;
     if (!fin) {
-      if (owner) put_part<MT>(p, band, sidx, col, v);
+      put_part<MT>(p, band, sidx, col, v);
       wait_vmem();
       __syncthreads();
       if (tid == 0) s_last = atomicAdd(&p.ctr[kCtrBand + band], 1) == nseg - 1;
       __syncthreads();
       fin = s_last;
       if (fin) {
-        if (owner) sum_parts<MT>(p, band, nseg, col, v);
+        sum_parts<MT>(p, band, nseg, col, v);
         if (tid == 0) store_dev(&p.ctr[kCtrBand + band], 0);
       }
     }
     if (fin) {
       if (rank) {
-        if (wave == 0) finish_rank<MT>(p, band, v);
+        finish_rank<MT>(p, band, v);
         wait_vmem();
         __syncthreads();
         if (tid == 0) atomicAdd(&p.ctr[kCtrRankDone], 1);
@@ -448,7 +466,6 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(DecodeParams p) {
         finish_row<MT>(p, band - p.RB, v);
       }
     }
-    __syncthreads();  // the LDS pool is reused by the next segment
   }
 
   if (p.RB > 0 && tid == 0) {
@@ -509,8 +526,9 @@ hipError_t launch_decode(const Shape& s, const LayerArgs& a, const WsPtrs& w, hi
   p.KB = s.KB();
   p.RB = pl.rank_bands;
   p.NB = pl.bands;
-  p.U = pl.units;
   p.P = pl.workgroups;
+  p.rank_cost = pl.rank_cost;
+  p.ctot = pl.cost;
   p.maxseg = pl.maxseg;
   if (s.T <= 16) return s.grouped ? go<1, true>(p, st) : go<1, false>(p, st);
   return s.grouped ? go<2, true>(p, st) : go<2, false>(p, st);

@@ -53,7 +53,7 @@ __global__ __launch_bounds__(256, 1) void prefill_kernel(PrefillParams p) {
   __shared__ float gx[2][kPrefillBM];   // block sum of x per token
 
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
+  const int lane = tid & 63, wave = wave_id();
   const int wm = wave >> 1, wn = wave & 1;
   const int i32 = lane & 31, q = lane >> 5;
 

@@ -41,7 +41,7 @@ __global__ __launch_bounds__(256, 2) void projection_kernel(ProjParams p) {
   constexpr int RA = RTX > 0 ? RTX : 1;  // array extent (rank 0 still sums x)
   __shared__ float red[4][MT][RTX + 1][4][64];
 
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63, wave = wave_id();
   const int q = lane >> 4, c16 = lane & 15;
   const int tile = blockIdx.x, split = blockIdx.y;
   const int KB = p.K / kBlockK;

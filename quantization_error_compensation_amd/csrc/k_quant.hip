@@ -55,7 +55,7 @@ __global__ __launch_bounds__(256) void quantize_rtn_kernel(const float* __restri
                                                            int g, int asym) {
   __shared__ uint8_t zb[1024];
   const int n = blockIdx.x;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63, wave = wave_id();
   const int G = K / g, words = g / 8;
   const float* row = w + (size_t)n * K;
   for (int j = wave; j < G; j += 4) {
