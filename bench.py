@@ -95,11 +95,18 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run one plain device copy of known size (for HBM counter scaling)")
+    ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="no GPU run: read the counter CSVs of two rocprofv3 --pmc runs of this "
+                         "script (FETCH_SIZE, then WRITE_SIZE, both with --copy-calibration) and "
+                         "write profiles/traffic_<config>.json")
     return ap.parse_args()
 
 
 def main():
     args = parse()
+    if args.traffic_from:
+        write_traffic(args)
+        return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -207,12 +214,13 @@ def main():
             return {"bound": "hbm", "achieved": round(c["gbs"], 1), "peak": HBM_PEAK_GBS,
                     "unit": "GB/s", "frac": round(c["gbs"] / HBM_PEAK_GBS, 4),
                     "traffic": traffic.get(f"decode_T{c['tokens']}"),
-                    "kernel": f"spear_ec_linear (decode, {c['tokens']} tokens): projection + decode kernels",
+                    "kernel": f"decode_kernel: the whole decode call ({c['tokens']} tokens) is this one launch",
                     "avg_us": round(c["ms"] * 1e3, 2)}
         return {"bound": "mfma", "achieved": round(c["tflops"], 1), "peak": BF16_PEAK_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(c["tflops"] / BF16_PEAK_TFLOPS, 4),
                 "traffic": traffic.get(f"prefill_T{c['tokens']}"),
-                "kernel": f"spear_ec_linear (prefill, {c['tokens']} tokens): projection + prefill kernels",
+                "kernel": f"prefill call ({c['tokens']} tokens): projection_kernel + finish_kernel + "
+                          "prefill_kernel, timed together between events on the launch stream",
                 "avg_us": round(c["ms"] * 1e3, 2)}
 
     head = dec[0] if dec else pre[0]
@@ -241,6 +249,64 @@ def main():
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(spec, r, plan, X, A, B, gv, bv, unit)
     print(json.dumps(out), flush=True)
+
+
+CALIB_BYTES = 1 << 28   # the --copy-calibration copy: 256 MiB read, 256 MiB written
+
+# Kernels of each call of the dispatcher (matched against the mangled names).
+CALL_KERNELS = {"decode": ("decode_kernel",),
+                "prefill": ("projection_kernel", "finish_kernel", "prefill_kernel")}
+
+
+def read_counter_csv(d, counter):
+    """Per-dispatch values of one counter from a rocprofv3 --pmc run written
+    with --output-format csv: [(kernel_name, grid_size, value), ...]."""
+    import csv
+    import glob
+    files = glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)
+    if not files:
+        raise SystemExit(f"no counter_collection.csv under {d}")
+    rows = []
+    for fn in files:
+        with open(fn) as f:
+            for r in csv.DictReader(f):
+                if r.get("Counter_Name") == counter:
+                    rows.append((r["Kernel_Name"], int(r.get("Grid_Size", 0) or 0),
+                                 float(r["Counter_Value"])))
+    return rows
+
+
+def write_traffic(args):
+    """HBM bytes per call from FETCH_SIZE / WRITE_SIZE (KiB per dispatch),
+    each scaled by what the same counter reads for the 256 MiB calibration
+    copy, averaged over the dispatches of each kernel of the call."""
+    spec_plan = WORKLOADS[args.config]["steps"]
+    out = {"config": args.config, "kernel_source_hash": kernel_source_hash(),
+           "calibration_bytes": CALIB_BYTES, "bytes_per_call": {}, "counters": {}}
+    per_kernel = {}
+    for d, counter in zip(args.traffic_from, ("FETCH_SIZE", "WRITE_SIZE")):
+        rows = read_counter_csv(d, counter)
+        copies = [v for k, g, v in rows if "copy" in k.lower() or "elementwise" in k.lower()]
+        if not copies:
+            raise SystemExit(f"{counter}: no copy kernel found for the calibration")
+        factor = CALIB_BYTES / (max(copies) * 1024.0)
+        out["counters"][counter] = {"calibration_kib": max(copies), "scale": factor}
+        for path, names in CALL_KERNELS.items():
+            for nm in names:
+                vals = [v for k, g, v in rows if nm in k]
+                if vals:
+                    per_kernel.setdefault(nm, {})[counter] = float(np.mean(vals)) * 1024.0 * factor
+    for path, T in spec_plan:
+        tot = 0.0
+        for nm in CALL_KERNELS[path]:
+            if nm in per_kernel:
+                tot += per_kernel[nm].get("FETCH_SIZE", 0.0) + per_kernel[nm].get("WRITE_SIZE", 0.0)
+        out["bytes_per_call"][f"{path}_T{T}"] = round(tot)
+    out["bytes_per_kernel"] = {k: {c: round(v) for c, v in d.items()} for k, d in per_kernel.items()}
+    dst = os.path.join(ROOT, "profiles", f"traffic_{args.config}.json")
+    with open(dst, "w") as f:
+        json.dump(out, f, indent=1)
+    print(json.dumps(out))
 
 
 def load_traffic(config):
