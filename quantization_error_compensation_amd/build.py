@@ -30,9 +30,16 @@ CFLAGS = [
 ]
 
 
+# Per-file flags.  The prefill GEMM folds its matrix-core accumulators with
+# vector instructions every K block; keeping the accumulators in ordinary
+# VGPRs (instead of the compiler's default AGPR placement) removes a copy of
+# every accumulator in and out of the AGPR file per block.
+FILE_FLAGS = {"k_prefill.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+
+
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD_DIR, os.path.splitext(src)[0] + ".o")
-    cmd = [HIPCC, *CFLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [HIPCC, *CFLAGS, *FILE_FLAGS.get(src, []), "-c", os.path.join(CSRC, src), "-o", obj]
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         raise RuntimeError(f"compile failed: {' '.join(cmd)}\n{res.stderr}")

@@ -71,7 +71,7 @@ Workspace layout(const Shape& s, bool decode) {
     const size_t Tp = (size_t)pp.tiles * kProjTokens;
     w.wvhi = o;   o = up256(o + 2 * T * r);
     w.wvlo = o;   o = up256(o + 2 * T * r);
-    w.sblk = o;   o = up256(o + sizeof(float) * (size_t)s.KB() * Tp);
+    w.sblk = o;   o = up256(o + 8 * (size_t)s.KB() * Tp);
     w.stot = o;   o = up256(o + sizeof(float) * Tp);
     // splits * T <= min(max(1, KB/4) * T, 16384 + T): a bound that grows with
     // T, so sizing for the largest token count covers every smaller one.
@@ -92,7 +92,7 @@ WsPtrs carve(void* base, const Workspace& w) {
   p.wv32 = reinterpret_cast<float*>(b + w.wv32);
   p.wvhi = reinterpret_cast<uint16_t*>(b + w.wvhi);
   p.wvlo = reinterpret_cast<uint16_t*>(b + w.wvlo);
-  p.sblk = reinterpret_cast<float*>(b + w.sblk);
+  p.sblk = reinterpret_cast<uint32_t*>(b + w.sblk);
   p.stot = reinterpret_cast<float*>(b + w.stot);
   p.upart = reinterpret_cast<float*>(b + w.upart);
   p.ypart = reinterpret_cast<float*>(b + w.ypart);

@@ -48,6 +48,23 @@ __device__ __forceinline__ u32x4 codes_to_bf16_offset(uint32_t w) {
   return o;
 }
 
+// Eight codes -> bf16 pairs of 128 + c in natural column order (c0,c1),
+// (c2,c3), (c4,c5), (c6,c7): the even and odd nibbles are split into bytes,
+// interleaved back into column order, then placed under the exponent byte.
+__device__ __forceinline__ u32x4 codes_to_bf16_offset_natural(uint32_t w) {
+  const uint32_t lo = w & 0x0F0F0F0Fu;                        // bytes: c0 c2 c4 c6
+  const uint32_t hi = (w >> 4) & 0x0F0F0F0Fu;                 // bytes: c1 c3 c5 c7
+  const uint32_t a = __builtin_amdgcn_perm(hi, lo, 0x05010400u);  // c0 c1 c2 c3
+  const uint32_t b = __builtin_amdgcn_perm(hi, lo, 0x07030602u);  // c4 c5 c6 c7
+  const uint32_t m = 0x43434343u;
+  u32x4 o;
+  o.x = __builtin_amdgcn_perm(a, m, 0x01050004u);  // (c0, c1)
+  o.y = __builtin_amdgcn_perm(a, m, 0x01070006u);  // (c2, c3)
+  o.z = __builtin_amdgcn_perm(b, m, 0x01050004u);  // (c4, c5)
+  o.w = __builtin_amdgcn_perm(b, m, 0x01070006u);  // (c6, c7)
+  return o;
+}
+
 // Eight consecutive bf16 activations (packed in 4 words) -> the same operand
 // order 0,2,4,6,1,3,5,7 as codes_to_bf16_offset.
 __device__ __forceinline__ u32x4 x_permute8(u32x4 d) {
@@ -116,6 +133,16 @@ __device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
 }
 __device__ __forceinline__ u32x4 bload16(rsrc_t r, uint32_t voff, uint32_t soff) {
   return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
+}
+// Loads straight into LDS (no registers): lane i's bytes land at
+// lds + size * i, so one instruction fills a contiguous run of LDS.  The
+// loads count in vmcnt like any other buffer load.
+typedef __attribute__((address_space(3))) void lds_void_t;
+__device__ __forceinline__ void bload16_lds(rsrc_t r, void* lds, uint32_t voff, uint32_t soff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t*)lds, 16, voff, soff, 0, 0);
+}
+__device__ __forceinline__ void bload4_lds(rsrc_t r, void* lds, uint32_t voff, uint32_t soff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t*)lds, 4, voff, soff, 0, 0);
 }
 __device__ __forceinline__ uint32_t bload4(rsrc_t r, uint32_t voff, uint32_t soff) {
   return (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0);

@@ -62,7 +62,7 @@ struct WsPtrs {
   float* wv32;     // [T][r]      alpha * gated projection
   uint16_t* wvhi;  // [T][r]      bf16 high part of alpha * v (prefill)
   uint16_t* wvlo;  // [T][r]      bf16 remainder (prefill)
-  float* sblk;     // [KB][Tp]    sum of x over each 128-column block (prefill)
+  uint32_t* sblk;  // [KB][Tp][2] sum of x over each 128-column block as bf16 hi|mid, lo (prefill)
   float* stot;     // [T]         sum of x over the whole row (prefill)
   float* upart;    // projection partials: prefill [splits][T][r+1], decode [splits][T][r]
   float* ypart;    // [splits][T][N] decode partials

@@ -10,15 +10,25 @@
 //
 // Tile: 128 tokens x 128 output rows per workgroup of 4 waves (2 x 2), each
 // wave 64 x 64 = 2 x 2 tiles of the 32x32x16 bf16 MFMA.  K advances in
-// 128-column blocks (one scale group when g = 128), double-buffered in LDS:
-//   x tile   128 x 128 bf16, each 8-column block stored in the operand order
-//            0,4,1,5,2,6,3,7 of the integer-code operands (row stride 272 B);
-//   W tile   128 rows x 64 B of packed codes (row stride 80 B).
-// A lane's weight operand for K step s is word 8*(lane/32) + s of its row;
-// the matching activations are 8-column block 8*(lane/32) + s of its token.
-// Group-wise scales: each block's partial products restart from zero and are
-// folded in with s * (P - (128 + z) * sum_x).  Per-channel: one chain over
-// all of K, corrected once at the end.
+// 128-column blocks (one scale group when g = 128) through a 3-stage LDS ring
+// filled by buffer loads that write LDS directly (no register staging); the
+// loads of block kb + 2 are in flight while block kb is multiplied, and one
+// barrier per block both publishes a stage and retires the oldest one.
+//   x stage  128 tokens x 256 B; 16-byte piece p of token t is stored at
+//            position p ^ (t & 15), so the fragment reads of 16 consecutive
+//            tokens hit 16 different bank groups;
+//   W stage  128 rows x 64 B of packed codes, piece p of row n at
+//            p ^ ((n >> 2) & 3) for the same reason;
+//   metadata per block: the 4-byte words holding each row's fp16 scale and
+//            zero-point nibble, and the block sums of x of each token (as
+//            three bf16 parts).
+// A lane's weight operand for K step s is word 8*(lane/32) + s of its row,
+// converted to 128 + c in natural column order; the matching activations are
+// 16-byte piece 8*(lane/32) + s of its token.  Group-wise scales: each
+// block's partial products P = sum (128 + c) x - (128 + z) sum_x restart
+// from zero (the offset term is one extra matrix-core step) and are folded
+// in with s * P.  Per-channel: one chain over all of K, corrected once at
+// the end.
 #include "common.hpp"
 #include "internal.hpp"
 
@@ -29,28 +39,31 @@ struct PrefillParams {
   const uint16_t* x;       // [T][K] bf16
   const uint32_t* wq;      // [N][K/8]
   const uint16_t* scales;  // [N][G]
-  const uint32_t* zeros;   // [N][ZW] or null
+  const uint32_t* zeros;   // [N][ZW], or the scales when has_z == 0 (never used then)
   const uint16_t* B;       // [N][r] bf16
   const uint16_t* wvhi;    // [T][r] bf16
   const uint16_t* wvlo;    // [T][r] bf16
-  const float* sblk;       // [KB][Tp]
+  const uint32_t* sblk;    // [KB][Tp][2] block sums of x, bf16 (hi | mid << 16, lo)
   const float* stot;       // [T]
   uint16_t* y;             // [T][N]
-  int T, K, N, r, Tp, G, ZW, tiles_m, tiles_n;
+  int T, K, N, r, Tp, G, ZW, has_z, tiles_m, tiles_n;
 };
 
-constexpr int XS = 272;   // x tile row stride in LDS (bytes)
-constexpr int WS = 80;    // W tile row stride in LDS (bytes)
-constexpr int XTILE = kPrefillBM * XS;
-constexpr int WTILE = kPrefillBN * WS;
+constexpr int kXStage = kPrefillBM * 256;           // 32 KB
+constexpr int kWStage = kPrefillBN * 64;            // 8 KB
+// metadata: scale words [128], zero-point words [128], sums of x [128][8 B],
+// and a spare area that keeps every wave's load count equal
+constexpr int kMStage = 512 + 512 + 1024 + 512;
+constexpr int kStage = kXStage + kWStage + kMStage;
+constexpr int kStages = 3;
+// Buffer loads each wave issues per block (8 x, 2 W, 2 metadata); the ring's
+// waits count on it.
+constexpr int kLoadsPerBlock = 12;
+static_assert(kLoadsPerBlock == 12, "s_waitcnt immediates below assume 12 loads per block");
 
 template <bool GROUPED>
 __global__ __launch_bounds__(256, 1) void prefill_kernel(PrefillParams p) {
-  __shared__ __attribute__((aligned(16))) uint8_t xs[2][XTILE];
-  __shared__ __attribute__((aligned(16))) uint8_t ws[2][WTILE];
-  __shared__ float gs[2][kPrefillBN];   // group scale per row
-  __shared__ float gz[2][kPrefillBN];   // -(128 + z) per row
-  __shared__ float gx[2][kPrefillBM];   // block sum of x per token
+  __shared__ __attribute__((aligned(16))) uint8_t smem[kStages * kStage];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = wave_id();
@@ -65,60 +78,45 @@ __global__ __launch_bounds__(256, 1) void prefill_kernel(PrefillParams p) {
   const int tn = tile / p.tiles_m, tm = tile % p.tiles_m;
   const int m0 = tm * kPrefillBM, n0 = tn * kPrefillBN;
   const int KB = p.K / kBlockK;
-  const size_t rowWords = (size_t)p.K / 8;
+  const int rows_m = min(kPrefillBM, p.T - m0), rows_n = min(kPrefillBN, p.N - n0);
 
-  // Cooperative global -> register -> LDS copy of one K block.
-  struct Regs {
-    u32x4 x[8];
-    u32x4 w[2];
-    float s, z, sx;
-  };
-  auto gload = [&](int kb, Regs& R) {
-    for (int c = 0; c < 8; ++c) {
-      const int chunk = tid + 256 * c, row = chunk >> 4, b8 = chunk & 15;
-      const int t = m0 + row;
-      R.x[c] = t < p.T ? load16(p.x + (size_t)t * p.K + (size_t)kb * kBlockK + 8 * b8)
-                       : u32x4{0, 0, 0, 0};
+  // Buffer views of this tile; rows past T or N read as zero.
+  const rsrc_t xr = make_rsrc(p.x + (size_t)m0 * p.K, (uint32_t)rows_m * p.K * 2);
+  const rsrc_t wr = make_rsrc(p.wq + (size_t)n0 * (p.K / 8), (uint32_t)rows_n * (p.K / 2));
+  // Scale words: a 4-byte aligned word around each 2-byte scale.  N is a
+  // multiple of 16, so rows_n * G * 2 is a multiple of 4 and the word never
+  // reaches past the tile's last scale.
+  const rsrc_t sr = make_rsrc(p.scales + (size_t)n0 * p.G, (uint32_t)rows_n * p.G * 2);
+  const rsrc_t zr = p.has_z ? make_rsrc(p.zeros + (size_t)n0 * p.ZW, (uint32_t)rows_n * p.ZW * 4)
+                            : sr;
+  const rsrc_t gr = make_rsrc(p.sblk, (uint32_t)KB * p.Tp * 8);
+
+  auto issue = [&](int kb, int stage) {
+    uint8_t* S = smem + stage * kStage;
+    for (int j = 0; j < 8; ++j) {  // x: tokens 32 wave + 4 j .. + 3
+      const int t = 32 * wave + 4 * j + (lane >> 4);
+      const uint32_t gp = (uint32_t)((lane & 15) ^ (t & 15));
+      bload16_lds(xr, S + (32 * wave + 4 * j) * 256, (uint32_t)t * p.K * 2 + gp * 16,
+                  (uint32_t)kb * 256);
     }
-    for (int c = 0; c < 2; ++c) {
-      const int chunk = tid + 256 * c, row = chunk >> 2, part = chunk & 3;
-      const int n = n0 + row;
-      R.w[c] = n < p.N ? load16(p.wq + (size_t)n * rowWords + (size_t)kb * 16 + 4 * part)
-                       : u32x4{0, 0, 0, 0};
+    for (int j = 0; j < 2; ++j) {  // W: rows 32 wave + 16 j .. + 15
+      const int n = 32 * wave + 16 * j + (lane >> 2);
+      const uint32_t gp = (uint32_t)((lane & 3) ^ ((n >> 2) & 3));
+      bload16_lds(wr, S + kXStage + (32 * wave + 16 * j) * 64, (uint32_t)n * (p.K / 2) + gp * 16,
+                  (uint32_t)kb * 64);
     }
-    if constexpr (GROUPED) {
-      if (tid < kPrefillBN) {
-        const int n = n0 + tid;
-        if (n < p.N) {
-          R.s = half_bits_to_f32(p.scales[(size_t)n * p.G + kb]);
-          const int z = p.zeros ? (int)((p.zeros[(size_t)n * p.ZW + kb / 8] >> (4 * (kb & 7))) & 15u) : 8;
-          R.z = -(float)(128 + z);
-        } else {
-          R.s = 0.f;
-          R.z = 0.f;
-        }
-      } else {
-        const int t = m0 + tid - kPrefillBN;
-        R.sx = t < p.T ? p.sblk[(size_t)kb * p.Tp + t] : 0.f;
-      }
-    }
-  };
-  auto sstore = [&](int stg, const Regs& R) {
-    for (int c = 0; c < 8; ++c) {
-      const int chunk = tid + 256 * c, row = chunk >> 4, b8 = chunk & 15;
-      *reinterpret_cast<u32x4*>(&xs[stg][row * XS + b8 * 16]) = x_permute8(R.x[c]);
-    }
-    for (int c = 0; c < 2; ++c) {
-      const int chunk = tid + 256 * c, row = chunk >> 2, part = chunk & 3;
-      *reinterpret_cast<u32x4*>(&ws[stg][row * WS + part * 16]) = R.w[c];
-    }
-    if constexpr (GROUPED) {
-      if (tid < kPrefillBN) {
-        gs[stg][tid] = R.s;
-        gz[stg][tid] = R.z;
-      } else {
-        gx[stg][tid - kPrefillBN] = R.sx;
-      }
+    uint8_t* M = S + kXStage + kWStage;
+    if (wave == 0) {  // scale words of rows 64 j + lane
+      for (int j = 0; j < 2; ++j)
+        bload4_lds(sr, M + 256 * j, (uint32_t)(((64 * j + lane) * p.G + kb) * 2) & ~3u, 0);
+    } else if (wave == 1) {  // zero-point words
+      for (int j = 0; j < 2; ++j)
+        bload4_lds(zr, M + 512 + 256 * j, (uint32_t)((64 * j + lane) * p.ZW + (kb >> 3)) * 4, 0);
+    } else if (wave == 2) {  // sums of x of tokens 2 lane, 2 lane + 1; one spare load
+      bload16_lds(gr, M + 1024, (uint32_t)(kb * p.Tp + m0 + 2 * lane) * 8, 0);
+      bload4_lds(sr, M + 2048, 0, 0);
+    } else {
+      for (int j = 0; j < 2; ++j) bload4_lds(sr, M + 2048 + 256 * j, 0, 0);
     }
   };
 
@@ -131,64 +129,79 @@ __global__ __launch_bounds__(256, 1) void prefill_kernel(PrefillParams p) {
         tot[a][b][v] = 0.f;
       }
 
-  auto compute = [&](int stg) {
+  auto compute = [&](int stage, int kb) {
+    const uint8_t* X = smem + stage * kStage;
+    const uint8_t* W = X + kXStage;
+    const uint8_t* M = W + kWStage;
     u32x4 wd[2][2];
     for (int ns = 0; ns < 2; ++ns) {
-      const int row = wn * 64 + ns * 32 + i32;
-      wd[ns][0] = *reinterpret_cast<const u32x4*>(&ws[stg][row * WS + q * 32]);
-      wd[ns][1] = *reinterpret_cast<const u32x4*>(&ws[stg][row * WS + q * 32 + 16]);
+      const int n = wn * 64 + ns * 32 + i32;
+      const int sw = (n >> 2) & 3;
+      wd[ns][0] = *reinterpret_cast<const u32x4*>(W + n * 64 + ((2 * q) ^ sw) * 16);
+      wd[ns][1] = *reinterpret_cast<const u32x4*>(W + n * 64 + ((2 * q + 1) ^ sw) * 16);
     }
+    float sc[2];
+    if constexpr (GROUPED) {
+      // Offset step: P starts at -(128 + z) * sum_x through one extra K = 16
+      // matrix-core step whose only non-zero terms are the three bf16 parts
+      // of sum_x (token side) against the exact bf16 value -(128 + z) (row
+      // side); then P gathers the eight code steps and is folded with s.
+      const uint32_t* Ms = reinterpret_cast<const uint32_t*>(M);
+      u32x4 xo[2], wo[2];
+      for (int ms = 0; ms < 2; ++ms) {
+        const int t = wm * 64 + ms * 32 + i32;
+        const u32x2 sx = *reinterpret_cast<const u32x2*>(M + 1024 + t * 8);
+        xo[ms] = q == 0 ? u32x4{sx.x, sx.y, 0u, 0u} : u32x4{0u, 0u, 0u, 0u};
+      }
+      for (int ns = 0; ns < 2; ++ns) {
+        const int n = wn * 64 + ns * 32 + i32;
+        const uint32_t sword = Ms[n];
+        const uint32_t sbits = (((n0 + n) * p.G + kb) & 1) ? (sword >> 16) : (sword & 0xFFFFu);
+        sc[ns] = half_bits_to_f32((uint16_t)sbits);
+        const uint32_t z = p.has_z ? (Ms[128 + n] >> (4 * (kb & 7))) & 15u : 8u;
+        const uint32_t mzb = 0xC300u | z;  // bf16 bits of -(128 + z)
+        wo[ns] = q == 0 ? u32x4{mzb | (mzb << 16), mzb, 0u, 0u} : u32x4{0u, 0u, 0u, 0u};
+      }
+      f32x16 zero;
+      for (int v = 0; v < 16; ++v) zero[v] = 0.f;
+      for (int ms = 0; ms < 2; ++ms)
+        for (int ns = 0; ns < 2; ++ns) acc[ms][ns] = mfma32x32x16(xo[ms], wo[ns], zero);
+    }
+#pragma unroll
     for (int s = 0; s < 8; ++s) {
       u32x4 xa[2], wb[2];
       for (int ms = 0; ms < 2; ++ms) {
-        const int row = wm * 64 + ms * 32 + i32;
-        xa[ms] = *reinterpret_cast<const u32x4*>(&xs[stg][row * XS + (8 * q + s) * 16]);
+        const int t = wm * 64 + ms * 32 + i32;
+        xa[ms] = *reinterpret_cast<const u32x4*>(X + t * 256 + ((8 * q + s) ^ (t & 15)) * 16);
       }
-      for (int ns = 0; ns < 2; ++ns) {
-        const u32x4 d = wd[ns][s >> 2];
-        const uint32_t word = (s & 3) == 0 ? d.x : (s & 3) == 1 ? d.y : (s & 3) == 2 ? d.z : d.w;
-        wb[ns] = codes_to_bf16_offset(word);
-      }
+      for (int ns = 0; ns < 2; ++ns) wb[ns] = codes_to_bf16_offset_natural(wd[ns][s >> 2][s & 3]);
       for (int ms = 0; ms < 2; ++ms)
-        for (int ns = 0; ns < 2; ++ns) {
-          if (GROUPED && s == 0) {
-            f32x16 zero;
-            for (int v = 0; v < 16; ++v) zero[v] = 0.f;
-            acc[ms][ns] = mfma32x32x16(xa[ms], wb[ns], zero);
-          } else {
-            acc[ms][ns] = mfma32x32x16(xa[ms], wb[ns], acc[ms][ns]);
-          }
-        }
+        for (int ns = 0; ns < 2; ++ns) acc[ms][ns] = mfma32x32x16(xa[ms], wb[ns], acc[ms][ns]);
     }
     if constexpr (GROUPED) {
-      for (int ns = 0; ns < 2; ++ns) {
-        const int nr = wn * 64 + ns * 32 + i32;
-        const float sc = gs[stg][nr], mz = gz[stg][nr];
-        for (int ms = 0; ms < 2; ++ms)
-          for (int v = 0; v < 16; ++v) {
-            const int tr = wm * 64 + ms * 32 + 8 * (v >> 2) + 4 * q + (v & 3);
-            tot[ms][ns][v] = fmaf(sc, fmaf(mz, gx[stg][tr], acc[ms][ns][v]), tot[ms][ns][v]);
-          }
-      }
+      for (int ms = 0; ms < 2; ++ms)
+        for (int ns = 0; ns < 2; ++ns)
+          for (int v = 0; v < 16; ++v) tot[ms][ns][v] = fmaf(sc[ns], acc[ms][ns][v], tot[ms][ns][v]);
     }
   };
 
-  // Main K loop: block kb+1 is loaded into registers while kb computes.
-  {
-    Regs R;
-    gload(0, R);
-    sstore(0, R);
-  }
-  __syncthreads();
+  // K loop over the 3-stage ring.  At the top of iteration kb this wave's
+  // loads of blocks kb and kb + 1 are in flight (12 each); waiting until at
+  // most 12 remain completes block kb, and the barrier makes every wave's
+  // part of it visible.  Past the barrier every wave has finished block
+  // kb - 1, so its stage takes the loads of block kb + 2.  Past the last
+  // block the loads repeat block KB - 1 into the free stage, which keeps the
+  // count of loads in flight the same in every iteration.
+  issue(0, 0);
+  issue(min(1, KB - 1), 1);
   for (int kb = 0; kb < KB; ++kb) {
-    const int cur = kb & 1;
-    Regs R;
-    const bool more = kb + 1 < KB;
-    if (more) gload(kb + 1, R);
-    compute(cur);
-    if (more) sstore(cur ^ 1, R);
-    __syncthreads();
+    asm volatile("s_waitcnt vmcnt(12)" ::: "memory");
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    issue(min(kb + 2, KB - 1), (kb + 2) % kStages);
+    compute(kb % kStages, kb);
   }
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
   // Epilogue: scales (per-channel), then + alpha * v B^T, then one bf16 store.
   if constexpr (!GROUPED) {
@@ -197,7 +210,7 @@ __global__ __launch_bounds__(256, 1) void prefill_kernel(PrefillParams p) {
       float sc = 0.f, mz = 0.f;
       if (n < p.N) {
         sc = half_bits_to_f32(p.scales[n]);
-        const int z = p.zeros ? (int)(p.zeros[(size_t)n * p.ZW] & 15u) : 8;
+        const int z = p.has_z ? (int)(p.zeros[(size_t)n * p.ZW] & 15u) : 8;
         mz = -(float)(128 + z);
       }
       for (int ms = 0; ms < 2; ++ms)
@@ -247,7 +260,8 @@ hipError_t launch_prefill(const Shape& s, const LayerArgs& a, const WsPtrs& w, h
   p.x = static_cast<const uint16_t*>(a.x);
   p.wq = a.wq;
   p.scales = a.scales;
-  p.zeros = a.zeros;
+  p.has_z = a.zeros != nullptr;
+  p.zeros = a.zeros ? a.zeros : reinterpret_cast<const uint32_t*>(a.scales);
   p.B = static_cast<const uint16_t*>(a.B);
   p.wvhi = w.wvhi;
   p.wvlo = w.wvlo;

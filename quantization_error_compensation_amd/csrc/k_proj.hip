@@ -6,8 +6,9 @@
 // (r/N of the main one), computed once per token:
 //     u[t,j]  = sum_k A[j,k] x[t,k]                   (matrix cores, fp32 acc)
 //     wv[t,j] = alpha * sigmoid(g[j] u[t,j] + b[j]) * u[t,j]
-// together with the per-128-column sums of x, which the prefill GEMM uses to
-// remove the +128 offset of its integer-code operands, and whole-row sums.
+// together with the per-128-column sums of x (as exact bf16 triples), which
+// the prefill GEMM uses to remove the +128 offset of its integer-code
+// operands, and whole-row sums.
 //
 // projection_kernel: one workgroup per (32-token tile, K split); the four
 // waves take contiguous runs of 128-column blocks; the split's partial u (and
@@ -27,7 +28,7 @@ struct ProjParams {
   const float* bv;     // [r]
   float alpha;
   float* upart;        // [splits][T][r + 1]
-  float* sblk;         // [KB][Tp]
+  uint32_t* sblk;      // [KB][Tp][2]: block sums of x as bf16 (hi | mid << 16, lo)
   float* stot;         // [T]
   float* wv32;         // [T][r]
   uint16_t* wvhi;      // [T][r]
@@ -77,13 +78,24 @@ __global__ __launch_bounds__(256, 2) void projection_kernel(ProjParams p) {
       for (int rt = 0; rt < RTX; ++rt)
         for (int i = 0; i < 4; ++i) u[mt][rt] = mfma16x16x32(xf[mt][i], af[rt][i], u[mt][rt]);
       ssum[mt] += sb;
-      // every column of the ones-product holds the row sum; column 0 stores it
+      // every column of the ones-product holds the row sum; column 0 stores
+      // it as three bf16 parts hi + mid + lo that add up to the fp32 sum
+      // exactly (the prefill GEMM feeds them to the matrix cores)
       if (c16 == 0) {
         const int t = t0 + 16 * mt + 4 * q;
-        f32x4 sv = sb;
-        for (int v = 0; v < 4; ++v)
-          if (t + v >= p.T) sv[v] = 0.f;
-        *reinterpret_cast<f32x4*>(p.sblk + (size_t)blk * p.Tp + t) = sv;
+        u32x4 tw[2];
+        for (int v = 0; v < 4; ++v) {
+          const float sv = t + v < p.T ? sb[v] : 0.f;
+          const uint32_t hi = f32_to_bf16_rne(sv);
+          const float r1 = sv - __uint_as_float(hi << 16);
+          const uint32_t mid = f32_to_bf16_rne(r1);
+          const uint32_t lo = f32_to_bf16_rne(r1 - __uint_as_float(mid << 16));
+          tw[v >> 1][2 * (v & 1)] = hi | (mid << 16);
+          tw[v >> 1][2 * (v & 1) + 1] = lo;
+        }
+        uint32_t* dst = p.sblk + ((size_t)blk * p.Tp + t) * 2;
+        *reinterpret_cast<u32x4*>(dst) = tw[0];
+        *reinterpret_cast<u32x4*>(dst + 4) = tw[1];
       }
     }
   }
