@@ -53,6 +53,35 @@ DecodePlan plan_decode(const Shape& s, int slots) {
   return pl;
 }
 
+static PrefillPlan prefill_plan_for(const Shape& s, int tiles_m) {
+  PrefillPlan pl;
+  pl.tiles_m = tiles_m;
+  pl.tiles_n = (s.N + kPrefillBN - 1) / kPrefillBN;
+  const int tiles = pl.tiles_m * pl.tiles_n;
+  pl.splits = 1;
+  if (tiles < kPrefillTarget) {
+    const int want = (kPrefillTarget + tiles - 1) / tiles;
+    pl.splits = std::max(1, std::min({8, want, s.KB() / 4}));
+  }
+  pl.partial_floats = pl.splits > 1
+                          ? (size_t)tiles * pl.splits * kPrefillWaves * 64 * 64
+                          : 0;
+  return pl;
+}
+
+PrefillPlan plan_prefill(const Shape& s) {
+  return prefill_plan_for(s, (s.T + kPrefillBM - 1) / kPrefillBM);
+}
+
+// Largest split-partial area of any token count up to T, so that a workspace
+// sized for T tokens serves every smaller call too.
+static size_t prefill_partials_bound(const Shape& s) {
+  size_t m = 0;
+  const int tm_max = (s.T + kPrefillBM - 1) / kPrefillBM;
+  for (int tm = 1; tm <= tm_max; ++tm) m = std::max(m, prefill_plan_for(s, tm).partial_floats);
+  return m;
+}
+
 static size_t up256(size_t v) { return (v + 255) & ~(size_t)255; }
 
 Workspace layout(const Shape& s, bool decode) {
@@ -79,7 +108,7 @@ Workspace layout(const Shape& s, bool decode) {
     const size_t parts = std::min(kb4 * T, (size_t)16384 + T);
     (void)pp;
     w.upart = o;  o = up256(o + sizeof(float) * parts * (r + 1));
-    w.ypart = o;
+    w.ypart = o;  o = up256(o + sizeof(float) * prefill_partials_bound(s));
   }
   w.total = o;
   return w;

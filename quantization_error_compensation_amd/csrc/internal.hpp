@@ -12,7 +12,9 @@ constexpr int kBlockK = 128;          // K block: one scale group (g = 128) or a
 constexpr int kDecodeBandRows = 64;   // output rows per decode workgroup
 constexpr int kProjTokens = 32;       // tokens per projection workgroup (prefill path)
 constexpr int kPrefillBM = 128;       // tokens per prefill tile
-constexpr int kPrefillBN = 128;       // output rows per prefill tile
+constexpr int kPrefillBN = 256;       // output rows per prefill tile
+constexpr int kPrefillWaves = 8;      // waves per prefill workgroup (2 x 4 of 64 x 64)
+constexpr int kPrefillTarget = 256;   // split K until a call has at least this many workgroups
 constexpr int kCounterSlots = 4096;   // int32 words at the head of the workspace
 
 // Decode counter words (all zero between calls).
@@ -20,6 +22,7 @@ constexpr int kCtrRankDone = 1;  // rank bands whose gated projection is publish
 constexpr int kCtrExit = 2;      // decode workgroups that have finished
 constexpr int kCtrError = 3;     // set to 1 if a workgroup saw an inconsistent workspace
 constexpr int kCtrBand = 64;       // [64, 64 + bands): arrivals per band (rank bands first)
+constexpr int kCtrTile = 64;       // [64, 64 + tiles): prefill split-K arrivals per output tile
 constexpr int kMaxSlots = 1024;    // bound on resident decode workgroups used for sizing
 
 struct Shape {
@@ -46,7 +49,16 @@ struct DecodePlan {
   int maxseg;      // bound on the workgroups sharing one band
 };
 
+// Work split of the prefill GEMM: output tiles of kPrefillBM x kPrefillBN,
+// each split over `splits` K ranges when the tiles alone would leave compute
+// units idle (the last of a tile's splits to finish sums them in split order).
+struct PrefillPlan {
+  int tiles_m, tiles_n, splits;
+  size_t partial_floats;  // workspace floats for split partials (0 if splits == 1)
+};
+
 ProjPlan plan_projection(const Shape& s);
+PrefillPlan plan_prefill(const Shape& s);
 // slots: workgroups the device keeps resident (2 per CU); sizing uses kMaxSlots.
 DecodePlan plan_decode(const Shape& s, int slots);
 
@@ -65,7 +77,7 @@ struct WsPtrs {
   uint32_t* sblk;  // [KB][Tp][2] sum of x over each 128-column block as bf16 hi|mid, lo (prefill)
   float* stot;     // [T]         sum of x over the whole row (prefill)
   float* upart;    // projection partials: prefill [splits][T][r+1], decode [splits][T][r]
-  float* ypart;    // [splits][T][N] decode partials
+  float* ypart;    // decode: [bands][maxseg][T][64]; prefill: split-K tile partials
 };
 WsPtrs carve(void* base, const Workspace& w);
 

@@ -8,16 +8,19 @@
 // matrix-core product accumulated into the same registers as the main GEMM
 // before the single store of y.
 //
-// Tile: 128 tokens x 128 output rows per workgroup of 4 waves (2 x 2), each
-// wave 64 x 64 = 2 x 2 tiles of the 32x32x16 bf16 MFMA.  K advances in
-// 128-column blocks (one scale group when g = 128) through a 3-stage LDS ring
-// filled by buffer loads that write LDS directly (no register staging); the
-// loads of block kb + 2 are in flight while block kb is multiplied, and one
-// barrier per block both publishes a stage and retires the oldest one.
+// Tile: 128 tokens x 256 output rows per workgroup of 8 waves (2 x 4), each
+// wave 64 x 64 = 2 x 2 tiles of the 32x32x16 bf16 MFMA.  The bf16 activations
+// are the expensive operand to move (256 B per token per 128-column block
+// against 64 B of codes per row), so the tile is wide in rows: 48 KB of
+// global->LDS traffic per 8.4 MFLOP.  K advances in 128-column blocks (one
+// scale group when g = 128) through a 3-stage LDS ring filled by buffer loads
+// that write LDS directly (no register staging); the loads of block kb + 2
+// are in flight while block kb is multiplied, and one barrier per block both
+// publishes a stage and retires the oldest one.
 //   x stage  128 tokens x 256 B; 16-byte piece p of token t is stored at
 //            position p ^ (t & 15), so the fragment reads of 16 consecutive
 //            tokens hit 16 different bank groups;
-//   W stage  128 rows x 64 B of packed codes, piece p of row n at
+//   W stage  256 rows x 64 B of packed codes, piece p of row n at
 //            p ^ ((n >> 2) & 3) for the same reason;
 //   metadata per block: the 4-byte words holding each row's fp16 scale and
 //            zero-point nibble, and the block sums of x of each token (as
@@ -29,6 +32,12 @@
 // from zero (the offset term is one extra matrix-core step) and are folded
 // in with s * P.  Per-channel: one chain over all of K, corrected once at
 // the end.
+//
+// Split K: when the output tiles alone are fewer than the compute units can
+// take, each tile's K range is split; every split but the last to finish
+// stores its partial tile at device scope and bumps the tile's counter, and
+// the last sums all partials in split order (deterministic) before the
+// epilogue.
 #include "common.hpp"
 #include "internal.hpp"
 
@@ -45,39 +54,49 @@ struct PrefillParams {
   const uint16_t* wvlo;    // [T][r] bf16
   const uint32_t* sblk;    // [KB][Tp][2] block sums of x, bf16 (hi | mid << 16, lo)
   const float* stot;       // [T]
+  float* part;             // [tiles][splits][8 waves][64 values][64 lanes] split partials
+  int* ctr;                // counter words
   uint16_t* y;             // [T][N]
-  int T, K, N, r, Tp, G, ZW, has_z, tiles_m, tiles_n;
+  int T, K, N, r, Tp, G, ZW, has_z, tiles_m, tiles_n, splits;
 };
 
-constexpr int kXStage = kPrefillBM * 256;           // 32 KB
-constexpr int kWStage = kPrefillBN * 64;            // 8 KB
-// metadata: scale words [128], zero-point words [128], sums of x [128][8 B],
+constexpr int kXStage = kPrefillBM * 256;  // 32 KB
+constexpr int kWStage = kPrefillBN * 64;   // 16 KB
+// metadata: scale words [256], zero-point words [256], sums of x [128][8 B],
 // and a spare area that keeps every wave's load count equal
-constexpr int kMStage = 512 + 512 + 1024 + 512;
+constexpr int kMScale = 0, kMZero = 1024, kMSum = 2048, kMSpare = 3072;
+constexpr int kMStage = kMSpare + 256;
 constexpr int kStage = kXStage + kWStage + kMStage;
 constexpr int kStages = 3;
-// Buffer loads each wave issues per block (8 x, 2 W, 2 metadata); the ring's
-// waits count on it.
-constexpr int kLoadsPerBlock = 12;
-static_assert(kLoadsPerBlock == 12, "s_waitcnt immediates below assume 12 loads per block");
+static_assert(kStages * kStage <= 160 * 1024, "LDS ring exceeds 160 KB");
+// Buffer loads each wave issues per block: 4 x, 2 W, 2 metadata.  The ring's
+// s_waitcnt immediate below assumes exactly this count.
+constexpr int kLoadsPerBlock = 8;
+static_assert(kLoadsPerBlock == 8, "the vmcnt immediate in the K loop assumes 8 loads per block");
+static_assert(kPrefillWaves == 8 && kPrefillBN == 256 && kPrefillBM == 128, "tile shape");
 
 template <bool GROUPED>
-__global__ __launch_bounds__(256, 1) void prefill_kernel(PrefillParams p) {
+__global__ __launch_bounds__(512, 1) void prefill_kernel(PrefillParams p) {
   __shared__ __attribute__((aligned(16))) uint8_t smem[kStages * kStage];
+  __shared__ int s_last;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = wave_id();
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = wave >> 2, wn = wave & 3;
   const int i32 = lane & 31, q = lane >> 5;
 
-  // Tiles are n-major so that a run of workgroups shares a W tile; runs are
-  // placed on one XCD (workgroups are dealt to the 8 XCDs round-robin).
-  const int ntiles = p.tiles_m * p.tiles_n;
-  int tile = blockIdx.x;
-  if ((ntiles & 7) == 0) tile = (blockIdx.x & 7) * (ntiles >> 3) + (blockIdx.x >> 3);
-  const int tn = tile / p.tiles_m, tm = tile % p.tiles_m;
+  // Workgroup -> (tile, split).  Splits of a tile are adjacent and tiles are
+  // n-major, so a run of workgroups shares a W tile; runs are placed on one
+  // XCD (workgroups are dealt to the 8 XCDs round-robin).
+  const int total = p.tiles_m * p.tiles_n * p.splits;
+  int idx = blockIdx.x;
+  if ((total & 7) == 0) idx = (blockIdx.x & 7) * (total >> 3) + (blockIdx.x >> 3);
+  const int tile = idx / p.splits, split = idx - tile * p.splits;
+  const int tn = tile / p.tiles_m, tm = tile - tn * p.tiles_m;
   const int m0 = tm * kPrefillBM, n0 = tn * kPrefillBN;
   const int KB = p.K / kBlockK;
+  const int kb0 = (int)((long long)KB * split / p.splits);
+  const int kb1 = (int)((long long)KB * (split + 1) / p.splits);
   const int rows_m = min(kPrefillBM, p.T - m0), rows_n = min(kPrefillBN, p.N - n0);
 
   // Buffer views of this tile; rows past T or N read as zero.
@@ -93,10 +112,10 @@ __global__ __launch_bounds__(256, 1) void prefill_kernel(PrefillParams p) {
 
   auto issue = [&](int kb, int stage) {
     uint8_t* S = smem + stage * kStage;
-    for (int j = 0; j < 8; ++j) {  // x: tokens 32 wave + 4 j .. + 3
-      const int t = 32 * wave + 4 * j + (lane >> 4);
+    for (int j = 0; j < 4; ++j) {  // x: tokens 16 wave + 4 j .. + 3
+      const int t = 16 * wave + 4 * j + (lane >> 4);
       const uint32_t gp = (uint32_t)((lane & 15) ^ (t & 15));
-      bload16_lds(xr, S + (32 * wave + 4 * j) * 256, (uint32_t)t * p.K * 2 + gp * 16,
+      bload16_lds(xr, S + (16 * wave + 4 * j) * 256, (uint32_t)t * p.K * 2 + gp * 16,
                   (uint32_t)kb * 256);
     }
     for (int j = 0; j < 2; ++j) {  // W: rows 32 wave + 16 j .. + 15
@@ -106,17 +125,16 @@ __global__ __launch_bounds__(256, 1) void prefill_kernel(PrefillParams p) {
                   (uint32_t)kb * 64);
     }
     uint8_t* M = S + kXStage + kWStage;
-    if (wave == 0) {  // scale words of rows 64 j + lane
-      for (int j = 0; j < 2; ++j)
-        bload4_lds(sr, M + 256 * j, (uint32_t)(((64 * j + lane) * p.G + kb) * 2) & ~3u, 0);
-    } else if (wave == 1) {  // zero-point words
-      for (int j = 0; j < 2; ++j)
-        bload4_lds(zr, M + 512 + 256 * j, (uint32_t)((64 * j + lane) * p.ZW + (kb >> 3)) * 4, 0);
-    } else if (wave == 2) {  // sums of x of tokens 2 lane, 2 lane + 1; one spare load
-      bload16_lds(gr, M + 1024, (uint32_t)(kb * p.Tp + m0 + 2 * lane) * 8, 0);
-      bload4_lds(sr, M + 2048, 0, 0);
+    if (wave < 4) {  // scale and zero-point words of rows 64 wave + lane
+      const int n = 64 * wave + lane;
+      bload4_lds(sr, M + kMScale + 256 * wave, (uint32_t)((n * p.G + kb) * 2) & ~3u, 0);
+      bload4_lds(zr, M + kMZero + 256 * wave, (uint32_t)(n * p.ZW + (kb >> 3)) * 4, 0);
+    } else if (wave == 4) {  // sums of x of tokens 2 lane, 2 lane + 1
+      bload16_lds(gr, M + kMSum, (uint32_t)(kb * p.Tp + m0 + 2 * lane) * 8, 0);
+      bload4_lds(sr, M + kMSpare, 0, 0);
     } else {
-      for (int j = 0; j < 2; ++j) bload4_lds(sr, M + 2048 + 256 * j, 0, 0);
+      bload4_lds(sr, M + kMSpare, 0, 0);
+      bload4_lds(sr, M + kMSpare, 0, 0);
     }
   };
 
@@ -146,11 +164,12 @@ __global__ __launch_bounds__(256, 1) void prefill_kernel(PrefillParams p) {
       // matrix-core step whose only non-zero terms are the three bf16 parts
       // of sum_x (token side) against the exact bf16 value -(128 + z) (row
       // side); then P gathers the eight code steps and is folded with s.
-      const uint32_t* Ms = reinterpret_cast<const uint32_t*>(M);
+      const uint32_t* Ms = reinterpret_cast<const uint32_t*>(M + kMScale);
+      const uint32_t* Mz = reinterpret_cast<const uint32_t*>(M + kMZero);
       u32x4 xo[2], wo[2];
       for (int ms = 0; ms < 2; ++ms) {
         const int t = wm * 64 + ms * 32 + i32;
-        const u32x2 sx = *reinterpret_cast<const u32x2*>(M + 1024 + t * 8);
+        const u32x2 sx = *reinterpret_cast<const u32x2*>(M + kMSum + t * 8);
         xo[ms] = q == 0 ? u32x4{sx.x, sx.y, 0u, 0u} : u32x4{0u, 0u, 0u, 0u};
       }
       for (int ns = 0; ns < 2; ++ns) {
@@ -158,7 +177,7 @@ __global__ __launch_bounds__(256, 1) void prefill_kernel(PrefillParams p) {
         const uint32_t sword = Ms[n];
         const uint32_t sbits = (((n0 + n) * p.G + kb) & 1) ? (sword >> 16) : (sword & 0xFFFFu);
         sc[ns] = half_bits_to_f32((uint16_t)sbits);
-        const uint32_t z = p.has_z ? (Ms[128 + n] >> (4 * (kb & 7))) & 15u : 8u;
+        const uint32_t z = p.has_z ? (Mz[n] >> (4 * (kb & 7))) & 15u : 8u;
         const uint32_t mzb = 0xC300u | z;  // bf16 bits of -(128 + z)
         wo[ns] = q == 0 ? u32x4{mzb | (mzb << 16), mzb, 0u, 0u} : u32x4{0u, 0u, 0u, 0u};
       }
@@ -186,22 +205,67 @@ __global__ __launch_bounds__(256, 1) void prefill_kernel(PrefillParams p) {
   };
 
   // K loop over the 3-stage ring.  At the top of iteration kb this wave's
-  // loads of blocks kb and kb + 1 are in flight (12 each); waiting until at
-  // most 12 remain completes block kb, and the barrier makes every wave's
-  // part of it visible.  Past the barrier every wave has finished block
-  // kb - 1, so its stage takes the loads of block kb + 2.  Past the last
-  // block the loads repeat block KB - 1 into the free stage, which keeps the
-  // count of loads in flight the same in every iteration.
-  issue(0, 0);
-  issue(min(1, KB - 1), 1);
-  for (int kb = 0; kb < KB; ++kb) {
-    asm volatile("s_waitcnt vmcnt(12)" ::: "memory");
+  // loads of blocks kb and kb + 1 are in flight (8 each); waiting until at
+  // most 8 remain completes block kb, and the barrier makes every wave's part
+  // of it visible.  Past the barrier every wave has finished block kb - 1, so
+  // its stage takes the loads of block kb + 2.  Past the last block the loads
+  // repeat block kb1 - 1 into the free stage, which keeps the count of loads
+  // in flight the same in every iteration.
+  issue(kb0, 0);
+  issue(min(kb0 + 1, kb1 - 1), 1);
+  for (int kb = kb0; kb < kb1; ++kb) {
+    const int i = kb - kb0;
+    asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
     __builtin_amdgcn_s_barrier();
-    issue(min(kb + 2, KB - 1), (kb + 2) % kStages);
-    compute(kb % kStages, kb);
+    issue(min(kb + 2, kb1 - 1), (i + 2) % kStages);
+    compute(i % kStages, kb);
   }
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+
+  if constexpr (!GROUPED) {
+    for (int ms = 0; ms < 2; ++ms)
+      for (int ns = 0; ns < 2; ++ns) tot[ms][ns] = acc[ms][ns];
+  }
+
+  // Split K: partial tiles meet at device scope; the last split sums them in
+  // split order.  Each lane owns 64 values; value e of wave w lives at
+  // part[((tile * splits + split) * 8 + w) * 4096 + e * 64 + lane].
+  if (p.splits > 1) {
+    const uint32_t tile_floats = kPrefillWaves * 4096;
+    const rsrc_t pr = make_rsrc(p.part + (size_t)tile * p.splits * tile_floats,
+                                (uint32_t)p.splits * tile_floats * 4);
+    const uint32_t mine = (uint32_t)(wave * 4096 + lane) * 4;
+    for (int ms = 0; ms < 2; ++ms)
+      for (int ns = 0; ns < 2; ++ns)
+        for (int v = 0; v < 16; ++v)
+          bstore_dev(pr, mine + (uint32_t)((ms * 2 + ns) * 16 + v) * 256,
+                     (uint32_t)split * tile_floats * 4, tot[ms][ns][v]);
+    wait_vmem();
+    __syncthreads();
+    if (tid == 0) s_last = atomicAdd(&p.ctr[kCtrTile + tile], 1) == p.splits - 1;
+    __syncthreads();
+    if (!s_last) return;
+    if (tid == 0) store_dev(&p.ctr[kCtrTile + tile], 0);
+    f32x16 sum[2][2];
+    for (int ms = 0; ms < 2; ++ms)
+      for (int ns = 0; ns < 2; ++ns)
+        for (int v = 0; v < 16; ++v) sum[ms][ns][v] = 0.f;
+    for (int sp = 0; sp < p.splits; ++sp) {
+      if (sp == split) {
+        for (int ms = 0; ms < 2; ++ms)
+          for (int ns = 0; ns < 2; ++ns) sum[ms][ns] += tot[ms][ns];
+      } else {
+        for (int ms = 0; ms < 2; ++ms)
+          for (int ns = 0; ns < 2; ++ns)
+            for (int v = 0; v < 16; ++v)
+              sum[ms][ns][v] += bload_dev(pr, mine + (uint32_t)((ms * 2 + ns) * 16 + v) * 256,
+                                          (uint32_t)sp * tile_floats * 4);
+      }
+    }
+    for (int ms = 0; ms < 2; ++ms)
+      for (int ns = 0; ns < 2; ++ns) tot[ms][ns] = sum[ms][ns];
+  }
 
   // Epilogue: scales (per-channel), then + alpha * v B^T, then one bf16 store.
   if constexpr (!GROUPED) {
@@ -217,7 +281,7 @@ __global__ __launch_bounds__(256, 1) void prefill_kernel(PrefillParams p) {
         for (int v = 0; v < 16; ++v) {
           const int t = m0 + wm * 64 + ms * 32 + 8 * (v >> 2) + 4 * q + (v & 3);
           const float st = t < p.T ? p.stot[t] : 0.f;
-          tot[ms][ns][v] = sc * fmaf(mz, st, acc[ms][ns][v]);
+          tot[ms][ns][v] = sc * fmaf(mz, st, tot[ms][ns][v]);
         }
     }
   }
@@ -256,6 +320,7 @@ __global__ __launch_bounds__(256, 1) void prefill_kernel(PrefillParams p) {
 
 hipError_t launch_prefill(const Shape& s, const LayerArgs& a, const WsPtrs& w, hipStream_t st) {
   const ProjPlan pp = plan_projection(s);
+  const PrefillPlan pl = plan_prefill(s);
   PrefillParams p;
   p.x = static_cast<const uint16_t*>(a.x);
   p.wq = a.wq;
@@ -267,6 +332,8 @@ hipError_t launch_prefill(const Shape& s, const LayerArgs& a, const WsPtrs& w, h
   p.wvlo = w.wvlo;
   p.sblk = w.sblk;
   p.stot = w.stot;
+  p.part = w.ypart;
+  p.ctr = w.counters;
   p.y = static_cast<uint16_t*>(a.y);
   p.T = s.T;
   p.K = s.K;
@@ -275,13 +342,14 @@ hipError_t launch_prefill(const Shape& s, const LayerArgs& a, const WsPtrs& w, h
   p.Tp = pp.tiles * kProjTokens;
   p.G = s.K / s.g;
   p.ZW = (p.G + 7) / 8;
-  p.tiles_m = (s.T + kPrefillBM - 1) / kPrefillBM;
-  p.tiles_n = (s.N + kPrefillBN - 1) / kPrefillBN;
-  const int grid = p.tiles_m * p.tiles_n;
+  p.tiles_m = pl.tiles_m;
+  p.tiles_n = pl.tiles_n;
+  p.splits = pl.splits;
+  const int grid = p.tiles_m * p.tiles_n * p.splits;
   if (s.grouped)
-    hipLaunchKernelGGL(prefill_kernel<true>, dim3(grid), dim3(256), 0, st, p);
+    hipLaunchKernelGGL(prefill_kernel<true>, dim3(grid), dim3(64 * kPrefillWaves), 0, st, p);
   else
-    hipLaunchKernelGGL(prefill_kernel<false>, dim3(grid), dim3(256), 0, st, p);
+    hipLaunchKernelGGL(prefill_kernel<false>, dim3(grid), dim3(64 * kPrefillWaves), 0, st, p);
   return hipGetLastError();
 }
 
