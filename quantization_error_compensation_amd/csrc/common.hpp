@@ -134,16 +134,68 @@ __device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
 __device__ __forceinline__ u32x4 bload16(rsrc_t r, uint32_t voff, uint32_t soff) {
   return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
 }
-// Loads straight into LDS (no registers): lane i's bytes land at
-// lds + size * i, so one instruction fills a contiguous run of LDS.  The
-// loads count in vmcnt like any other buffer load.
-typedef __attribute__((address_space(3))) void lds_void_t;
-__device__ __forceinline__ void bload16_lds(rsrc_t r, void* lds, uint32_t voff, uint32_t soff) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t*)lds, 16, voff, soff, 0, 0);
+// Loads straight into LDS (no registers on the way), issued from inline
+// assembly.  The compiler tracks the LDS writes of its builtin form of these
+// loads and, unable to tell ring stages apart, waits for every such load
+// still in flight before any LDS read; a kernel that pipelines stages through
+// LDS then stalls on the stage it has just issued.  These forms are invisible
+// to that tracking: the kernel orders them itself with s_waitcnt vmcnt and a
+// barrier before it reads a stage.  They count in vmcnt like every vector
+// memory load.  M0 (the LDS base of the load) is saved and restored.
+//
+// Buffer descriptor as four scalar words: base, stride 0, byte count (loads
+// at offsets past it return zero), raw dword format.
+__device__ __forceinline__ u32x4 sdesc(const void* base, uint32_t bytes) {
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  u32x4 d;
+  d.x = __builtin_amdgcn_readfirstlane((uint32_t)a);
+  d.y = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
+  d.z = __builtin_amdgcn_readfirstlane(bytes);
+  d.w = 0x00020000u;
+  return d;
 }
-__device__ __forceinline__ void bload4_lds(rsrc_t r, void* lds, uint32_t voff, uint32_t soff) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t*)lds, 4, voff, soff, 0, 0);
+// Byte address in the workgroup's LDS of a pointer into __shared__ memory.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  uint32_t a = __builtin_amdgcn_readfirstlane(
+      (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p);
+  asm("" : "+s"(a));  // held in a register: a folded constant is no valid operand below
+  return a;
 }
+// Lane i's 16 (or 4) bytes at desc + off land at LDS address lds + 16 i (or
+// 4 i); lds must be wave-uniform (it is read from the first lane).  The
+// whole offset is the per-lane one, so every byte is checked against the
+// descriptor's range (past it: zero).
+__device__ __forceinline__ void dma16(u32x4 desc, uint32_t lds, uint32_t off) {
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %1\n\t"
+      "s_nop 0\n\t"
+      "buffer_load_dwordx4 %2, %3, 0 offen lds\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "s"(__builtin_amdgcn_readfirstlane(lds)), "v"(off), "s"(desc)
+      : "memory");
+}
+__device__ __forceinline__ void dma4(u32x4 desc, uint32_t lds, uint32_t off) {
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %1\n\t"
+      "s_nop 0\n\t"
+      "buffer_load_dword %2, %3, 0 offen lds\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "s"(__builtin_amdgcn_readfirstlane(lds)), "v"(off), "s"(desc)
+      : "memory");
+}
+// Wait until at most N of this wave's vector memory loads are in flight.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
 __device__ __forceinline__ uint32_t bload4(rsrc_t r, uint32_t voff, uint32_t soff) {
   return (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0);
 }

@@ -69,10 +69,8 @@ constexpr int kMStage = kMSpare + 256;
 constexpr int kStage = kXStage + kWStage + kMStage;
 constexpr int kStages = 3;
 static_assert(kStages * kStage <= 160 * 1024, "LDS ring exceeds 160 KB");
-// Buffer loads each wave issues per block: 4 x, 2 W, 2 metadata.  The ring's
-// s_waitcnt immediate below assumes exactly this count.
+// Loads into LDS each wave issues per block: 4 x, 2 W, 2 metadata.
 constexpr int kLoadsPerBlock = 8;
-static_assert(kLoadsPerBlock == 8, "the vmcnt immediate in the K loop assumes 8 loads per block");
 static_assert(kPrefillWaves == 8 && kPrefillBN == 256 && kPrefillBM == 128, "tile shape");
 
 template <bool GROUPED>
@@ -100,42 +98,42 @@ __global__ __launch_bounds__(512, 1) void prefill_kernel(PrefillParams p) {
   const int rows_m = min(kPrefillBM, p.T - m0), rows_n = min(kPrefillBN, p.N - n0);
 
   // Buffer views of this tile; rows past T or N read as zero.
-  const rsrc_t xr = make_rsrc(p.x + (size_t)m0 * p.K, (uint32_t)rows_m * p.K * 2);
-  const rsrc_t wr = make_rsrc(p.wq + (size_t)n0 * (p.K / 8), (uint32_t)rows_n * (p.K / 2));
+  const u32x4 xr = sdesc(p.x + (size_t)m0 * p.K, (uint32_t)rows_m * p.K * 2);
+  const u32x4 wr = sdesc(p.wq + (size_t)n0 * (p.K / 8), (uint32_t)rows_n * (p.K / 2));
   // Scale words: a 4-byte aligned word around each 2-byte scale.  N is a
   // multiple of 16, so rows_n * G * 2 is a multiple of 4 and the word never
   // reaches past the tile's last scale.
-  const rsrc_t sr = make_rsrc(p.scales + (size_t)n0 * p.G, (uint32_t)rows_n * p.G * 2);
-  const rsrc_t zr = p.has_z ? make_rsrc(p.zeros + (size_t)n0 * p.ZW, (uint32_t)rows_n * p.ZW * 4)
-                            : sr;
-  const rsrc_t gr = make_rsrc(p.sblk, (uint32_t)KB * p.Tp * 8);
+  const u32x4 sr = sdesc(p.scales + (size_t)n0 * p.G, (uint32_t)rows_n * p.G * 2);
+  const u32x4 zr = p.has_z ? sdesc(p.zeros + (size_t)n0 * p.ZW, (uint32_t)rows_n * p.ZW * 4) : sr;
+  const u32x4 gr = sdesc(p.sblk, (uint32_t)KB * p.Tp * 8);
+  const uint32_t lds0 = lds_addr(smem);
 
   auto issue = [&](int kb, int stage) {
-    uint8_t* S = smem + stage * kStage;
+    const uint32_t S = lds0 + stage * kStage;
     for (int j = 0; j < 4; ++j) {  // x: tokens 16 wave + 4 j .. + 3
       const int t = 16 * wave + 4 * j + (lane >> 4);
       const uint32_t gp = (uint32_t)((lane & 15) ^ (t & 15));
-      bload16_lds(xr, S + (16 * wave + 4 * j) * 256, (uint32_t)t * p.K * 2 + gp * 16,
-                  (uint32_t)kb * 256);
+      dma16(xr, S + (16 * wave + 4 * j) * 256,
+            (uint32_t)t * p.K * 2 + gp * 16 + (uint32_t)kb * 256);
     }
     for (int j = 0; j < 2; ++j) {  // W: rows 32 wave + 16 j .. + 15
       const int n = 32 * wave + 16 * j + (lane >> 2);
       const uint32_t gp = (uint32_t)((lane & 3) ^ ((n >> 2) & 3));
-      bload16_lds(wr, S + kXStage + (32 * wave + 16 * j) * 64, (uint32_t)n * (p.K / 2) + gp * 16,
-                  (uint32_t)kb * 64);
+      dma16(wr, S + kXStage + (32 * wave + 16 * j) * 64,
+            (uint32_t)n * (p.K / 2) + gp * 16 + (uint32_t)kb * 64);
     }
-    uint8_t* M = S + kXStage + kWStage;
-    if (wave < 4) {  // scale and zero-point words of rows 64 wave + lane
-      const int n = 64 * wave + lane;
-      bload4_lds(sr, M + kMScale + 256 * wave, (uint32_t)((n * p.G + kb) * 2) & ~3u, 0);
-      bload4_lds(zr, M + kMZero + 256 * wave, (uint32_t)(n * p.ZW + (kb >> 3)) * 4, 0);
-    } else if (wave == 4) {  // sums of x of tokens 2 lane, 2 lane + 1
-      bload16_lds(gr, M + kMSum, (uint32_t)(kb * p.Tp + m0 + 2 * lane) * 8, 0);
-      bload4_lds(sr, M + kMSpare, 0, 0);
-    } else {
-      bload4_lds(sr, M + kMSpare, 0, 0);
-      bload4_lds(sr, M + kMSpare, 0, 0);
-    }
+    // Metadata, two 4-byte loads per wave with no branch (the same count in
+    // every wave): waves 0-3 the scale and zero-point words of rows
+    // 64 w + lane; waves 4-7 a quarter each of the sums of x of the tile's
+    // 128 tokens, plus a load into a spare area.
+    const uint32_t M = S + kXStage + kWStage;
+    const bool low = wave < 4;
+    const int j = wave & 3, n = 64 * j + lane;
+    dma4(low ? sr : gr, M + (low ? kMScale : kMSum) + 256 * j,
+         low ? ((uint32_t)((n * p.G + kb) * 2) & ~3u)
+             : (uint32_t)(kb * p.Tp + m0) * 8 + 256 * j + 4 * lane);
+    dma4(low ? zr : sr, M + (low ? kMZero + 256 * j : kMSpare),
+         low ? (uint32_t)(n * p.ZW + (kb >> 3)) * 4 : 0u);
   };
 
   f32x16 acc[2][2];
@@ -215,9 +213,10 @@ __global__ __launch_bounds__(512, 1) void prefill_kernel(PrefillParams p) {
   issue(min(kb0 + 1, kb1 - 1), 1);
   for (int kb = kb0; kb < kb1; ++kb) {
     const int i = kb - kb0;
-    asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+    wait_vmcnt<kLoadsPerBlock>();
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
     __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
     issue(min(kb + 2, kb1 - 1), (i + 2) % kStages);
     compute(i % kStages, kb);
   }
