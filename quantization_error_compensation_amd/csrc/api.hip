@@ -39,7 +39,9 @@ DecodePlan plan_decode(const Shape& s, int slots) {
   const int ranks = std::min(std::max(s.r, 1), 64);
   pl.rank_cost = std::max(1, (5 * ranks + 63) / 64);
   pl.cost = (long long)pl.rank_bands * KB * pl.rank_cost + (long long)pl.bands * KB;
-  // At least 8 cost units (one burst of row blocks) per workgroup.
+  // At least 8 cost units (one burst of row blocks) per workgroup.  Since a
+  // rank unit costs at most 5, every workgroup's run then holds at least one
+  // unit, which the kernel's count of the workgroups sharing a band relies on.
   auto wgs = [&](int sl) {
     long long P = std::min<long long>(sl, std::max<long long>(1, pl.cost / 8));
     return (int)std::max<long long>(1, std::min<long long>(P, pl.units));
@@ -94,7 +96,8 @@ Workspace layout(const Shape& s, bool decode) {
     const DecodePlan dp = plan_decode(s, kMaxSlots);
     w.wvhi = w.wvlo = w.sblk = w.stot = w.upart = o;
     w.ypart = o;
-    o = up256(o + sizeof(float) * (size_t)(dp.bands + dp.rank_bands) * dp.maxseg * T * 64);
+    const size_t T4 = (T + 3) & ~(size_t)3;  // tokens rounded up to a multiple of 4
+    o = up256(o + sizeof(float) * (size_t)(dp.bands + dp.rank_bands) * dp.maxseg * T4 * 64);
   } else {
     const ProjPlan pp = plan_projection(s);
     const size_t Tp = (size_t)pp.tiles * kProjTokens;

@@ -224,8 +224,15 @@ constexpr int kDeviceScope = 16;  // buffer cache-policy bits: sc1
 __device__ __forceinline__ float bload_dev(rsrc_t r, uint32_t voff, uint32_t soff) {
   return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, kDeviceScope));
 }
+__device__ __forceinline__ u32x4 bload16_dev(rsrc_t r, uint32_t voff, uint32_t soff) {
+  return __builtin_bit_cast(u32x4,
+                            __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, kDeviceScope));
+}
 __device__ __forceinline__ void bstore_dev(rsrc_t r, uint32_t voff, uint32_t soff, float v) {
   __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), r, voff, soff, kDeviceScope);
+}
+__device__ __forceinline__ void bstore16_dev(rsrc_t r, uint32_t voff, uint32_t soff, f32x4 v) {
+  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), r, voff, soff, kDeviceScope);
 }
 
 // Plain global loads from a wave-uniform base plus a 32-bit byte offset (the

@@ -46,7 +46,7 @@ struct DecodePlan {
   int rank_cost;   // cost of one rank unit (a row unit costs 1)
   long long cost;  // total cost of all units
   int workgroups;  // persistent workgroups, each a run of units of equal cost
-  int maxseg;      // bound on the workgroups sharing one band
+  int maxseg;      // bound on the workgroups sharing one band (any P up to kMaxSlots)
 };
 
 // Work split of the prefill GEMM: output tiles of kPrefillBM x kPrefillBN,
@@ -77,7 +77,7 @@ struct WsPtrs {
   uint32_t* sblk;  // [KB][Tp][2] sum of x over each 128-column block as bf16 hi|mid, lo (prefill)
   float* stot;     // [T]         sum of x over the whole row (prefill)
   float* upart;    // projection partials: prefill [splits][T][r+1], decode [splits][T][r]
-  float* ypart;    // decode: [bands][maxseg][T][64]; prefill: split-K tile partials
+  float* ypart;    // decode: [bands][maxseg][64][T4] (T4: T rounded up to 4); prefill: split-K tile partials
 };
 WsPtrs carve(void* base, const Workspace& w);
 

@@ -18,6 +18,9 @@
 //
 // Inside a segment the four waves of a workgroup own one 16-row tile each
 // and walk the same K blocks in bursts of NS blocks:
+//   * in row bands every load of a burst (x, codes, metadata) is issued one
+//     burst ahead, into registers, so it is in flight while the previous
+//     burst computes;
 //   * x of the burst is loaded once per workgroup (each wave 4 tokens x
 //     256 B per instruction, full cache lines), permuted into the
 //     matrix-core K order and written to a double-buffered LDS area; one
@@ -53,7 +56,7 @@ struct DecodeParams {
   const float* gv;         // [r]
   const float* bv;         // [r]
   float alpha;
-  float* part;             // [bands][maxseg][T][64] partial sums
+  float* part;             // [bands][maxseg][64][T4] partial sums
   float* wv32;             // [T][r] alpha * v
   int* ctr;                // counter words
   uint16_t* y;             // [T][N] bf16
@@ -101,8 +104,11 @@ __device__ __forceinline__ int owner_of(const DecodeParams& p, long long u) {
 // ------------------------------------------------------------- x staging
 // x of blocks [b, b + NS) into an LDS buffer [NS][16*MT tokens][XROW], each
 // 16-byte piece already in the matrix-core K order.  Wave w loads tokens
-// 4w + 16m .. +3 (lane: token 4w + 16m + l/16, piece l%16); a wave whose
-// tokens all lie past T skips its loads and writes zeros.
+// 4w + 16m .. +3 (lane: token 4w + 16m + l/16, piece l%16).  Every wave
+// issues the same loads whatever T is, so the count of loads in flight, and
+// with it every wait, is path-independent: lanes of tokens past T, and all
+// lanes when live is false, load from past the end of the buffer, which
+// reads zeros without a memory access.
 template <int MT, int NS>
 struct XStage {
   u32x4 g[NS][MT];
@@ -110,18 +116,13 @@ struct XStage {
 
 template <int MT, int NS>
 __device__ __forceinline__ void x_issue(const DecodeParams& p, int wave, int lane, int b, int hi,
-                                        XStage<MT, NS>& s) {
+                                        bool live, XStage<MT, NS>& s) {
   const uint32_t xrowB = (uint32_t)p.K * 2;
+  const rsrc_t xr = make_rsrc(p.x, (uint32_t)p.T * xrowB);
   for (int m = 0; m < MT; ++m) {
-    const int t0 = 4 * wave + 16 * m;
-    // tokens past T load token T - 1: their products land in output rows
-    // that are never stored
-    const uint32_t vo = (uint32_t)min(t0 + (lane >> 4), p.T - 1) * xrowB + 16u * (lane & 15);
-    if (t0 < p.T) {
-      for (int i = 0; i < NS; ++i) s.g[i][m] = gload16(p.x, vo + (uint32_t)min(b + i, hi - 1) * 256);
-    } else {
-      for (int i = 0; i < NS; ++i) s.g[i][m] = u32x4{0u, 0u, 0u, 0u};
-    }
+    const int t = 4 * wave + 16 * m + (lane >> 4);
+    const uint32_t vo = live && t < p.T ? (uint32_t)t * xrowB + 16u * (lane & 15) : 0x80000000u;
+    for (int i = 0; i < NS; ++i) s.g[i][m] = bload16(xr, vo, (uint32_t)min(b + i, hi - 1) * 256);
   }
 }
 
@@ -165,7 +166,7 @@ __device__ void rank_segment(const DecodeParams& p, int rb, int lo, int hi, uint
   for (int b = lo; b < hi; b += NS, ++burst) {
     uint8_t* buf = xlds + (burst & 1) * Burst<MT>::kBuf;
     XStage<MT, NS> xsg;
-    x_issue<MT, NS>(p, wave, lane, b, hi, xsg);
+    x_issue<MT, NS>(p, wave, lane, b, hi, true, xsg);
     u32x4 a[NS][4];
     for (int i = 0; i < NS; ++i)
       for (int j = 0; j < 4; ++j)
@@ -196,6 +197,25 @@ __device__ void rank_segment(const DecodeParams& p, int rb, int lo, int hi, uint
 constexpr int kMetaChunk = 32;
 constexpr int kMetaWave = 16 * kMetaChunk * 2 + 16 * 8 * 4;  // bytes per wave
 
+// What one burst of a row segment takes from memory: x (permuted into LDS
+// when the burst starts), the codes, and at the start of a metadata chunk the
+// chunk's scales and zero-points.  Each burst's loads are issued one burst
+// ahead, so they are in flight while the previous burst computes.
+template <int MT, int NS>
+struct RowStage {
+  XStage<MT, NS> x;
+  u32x4 w[NS];
+  uint32_t sv[8], zv[2];
+};
+
+// A barrier that leaves global loads in flight: only this wave's LDS writes
+// are awaited before the workgroup meets.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
 // Rows 64 band + 16 wave + c16 (this wave's tile), blocks [lo, hi): partial
 // y with the scales applied.
 template <int MT, bool GROUPED>
@@ -207,7 +227,7 @@ __device__ void row_segment(const DecodeParams& p, int band, int lo, int hi, uin
   // a multiple of 64) reads the last tile again and stores nothing.
   const int rc = min(band * 64 + 16 * wave, p.N - 16);
   const uint32_t wrowB = (uint32_t)p.K / 2;
-  const uint32_t* Wt = p.wq + (size_t)rc * (p.K / 8);
+  const rsrc_t wr = make_rsrc(p.wq + (size_t)rc * (p.K / 8), 16u * wrowB);
   const uint32_t wo = (uint32_t)c16 * wrowB + 16u * q;
   const uint16_t* St = p.scales + (size_t)rc * p.G;
   const uint32_t* Zt = p.zeros + (size_t)rc * p.ZW;
@@ -219,42 +239,45 @@ __device__ void row_segment(const DecodeParams& p, int band, int lo, int hi, uin
   f32x4 acc[MT], ssum[MT];
   for (int mt = 0; mt < MT; ++mt) acc[mt] = ssum[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  for (int b = lo; b < hi; b += NS, ++burst) {
-    uint8_t* buf = xlds + (burst & 1) * Burst<MT>::kBuf;
-    uint32_t sv[8], zv[2];
-    const bool stage = GROUPED && (b - lo) % kMetaChunk == 0;
-    if (stage) {
-      c0 = b;
-      w0 = b >> 3;
+  auto issue = [&](RowStage<MT, NS>& s, int b) {
+    if (GROUPED && (b - lo) % kMetaChunk == 0) {
       const int c1 = min(b + kMetaChunk, hi);
-      const int blk = min(c0 + (lane & 31), c1 - 1);
+      const int blk = min(b + (lane & 31), c1 - 1);
       for (int k = 0; k < 8; ++k)
-        sv[k] = gload2(St, (uint32_t)((2 * k + (lane >> 5)) * p.G + blk) * 2);
+        s.sv[k] = gload2(St, (uint32_t)((2 * k + (lane >> 5)) * p.G + blk) * 2);
       for (int e = 0; e < 2; ++e) {
-        const int wd = min(w0 + (lane & 3) + 4 * e, (c1 - 1) >> 3);
-        zv[e] = p.has_z ? gload4(Zt, (uint32_t)((lane >> 2) * p.ZW + wd) * 4) : 0x88888888u;
+        const int wd = min((b >> 3) + (lane & 3) + 4 * e, (c1 - 1) >> 3);
+        s.zv[e] = p.has_z ? gload4(Zt, (uint32_t)((lane >> 2) * p.ZW + wd) * 4) : 0x88888888u;
       }
     }
-    XStage<MT, NS> xsg;
-    x_issue<MT, NS>(p, wave, lane, b, hi, xsg);
-    u32x4 w[NS];
-    for (int i = 0; i < NS; ++i) w[i] = gload16(Wt, wo + (uint32_t)min(b + i, hi - 1) * 64);
-    if (stage) {
-      for (int k = 0; k < 8; ++k) ms[(2 * k + (lane >> 5)) * kMetaChunk + (lane & 31)] = (uint16_t)sv[k];
-      for (int e = 0; e < 2; ++e) mz[(lane >> 2) * 8 + (lane & 3) + 4 * e] = zv[e];
+    const bool live = b < hi;  // a burst past the segment loads nothing
+    x_issue<MT, NS>(p, wave, lane, b, hi, live, s.x);
+    const uint32_t wv = live ? wo : 0x80000000u;
+    for (int i = 0; i < NS; ++i) s.w[i] = bload16(wr, wv, (uint32_t)min(b + i, hi - 1) * 64);
+  };
+
+  auto consume = [&](RowStage<MT, NS>& s, int b) {
+    uint8_t* buf = xlds + (burst & 1) * Burst<MT>::kBuf;
+    ++burst;
+    if (GROUPED && (b - lo) % kMetaChunk == 0) {
+      c0 = b;
+      w0 = b >> 3;
+      for (int k = 0; k < 8; ++k)
+        ms[(2 * k + (lane >> 5)) * kMetaChunk + (lane & 31)] = (uint16_t)s.sv[k];
+      for (int e = 0; e < 2; ++e) mz[(lane >> 2) * 8 + (lane & 3) + 4 * e] = s.zv[e];
     }
-    x_store<MT, NS>(buf, wave, lane, xsg);
-    __syncthreads();
+    x_store<MT, NS>(buf, wave, lane, s.x);
+    lds_barrier();
 #pragma unroll
     for (int i = 0; i < NS; ++i) {
       if (b + i >= hi) continue;
       u32x4 xf[MT][4];
       x_frags<MT>(buf, i, lane, xf);
       u32x4 wb[4];
-      wb[0] = codes_to_bf16_offset(w[i].x);
-      wb[1] = codes_to_bf16_offset(w[i].y);
-      wb[2] = codes_to_bf16_offset(w[i].z);
-      wb[3] = codes_to_bf16_offset(w[i].w);
+      wb[0] = codes_to_bf16_offset(s.w[i].x);
+      wb[1] = codes_to_bf16_offset(s.w[i].y);
+      wb[2] = codes_to_bf16_offset(s.w[i].z);
+      wb[3] = codes_to_bf16_offset(s.w[i].w);
       if constexpr (GROUPED) {
         const int blk = b + i;
         const float sc = half_bits_to_f32(ms[c16 * kMetaChunk + (blk - c0)]);
@@ -277,6 +300,21 @@ __device__ void row_segment(const DecodeParams& p, int band, int lo, int hi, uin
           }
       }
     }
+  };
+
+  // Two stages in turn: while one burst computes, the next one loads.  The
+  // stage past the segment's last burst is issued too, with its loads out of
+  // range (no memory access): the number of loads in flight is then the same
+  // on every path, so the waits on each stage stay exact.
+  RowStage<MT, NS> s0, s1;
+  issue(s0, lo);
+  for (int b = lo;; b += 2 * NS) {
+    issue(s1, b + NS);
+    consume(s0, b);
+    if (b + NS >= hi) break;
+    issue(s0, b + 2 * NS);
+    consume(s1, b + NS);
+    if (b + 2 * NS >= hi) break;
   }
 
   if constexpr (!GROUPED) {  // per-channel: one scale and one offset correction per row
@@ -291,11 +329,18 @@ __device__ void row_segment(const DecodeParams& p, int band, int lo, int hi, uin
 }
 
 // ------------------------------------------------------------ partial sums
-// [maxseg][T][64] floats per band, written and read at device scope.  Column
-// c of a partial is row 64 band + c of a row band, or rank 64 rb + c.
+// [maxseg][64 columns][T4] floats per band (T4: T rounded up to a multiple
+// of 4), written and read at device scope; a lane's four tokens of one
+// column form one 16-byte word, and words holding no token below T are
+// neither stored nor loaded.  Column c of a partial is row 64 band + c of a
+// row band, or rank 64 rb + c.
+__device__ __forceinline__ int tokens4(const DecodeParams& p) { return (p.T + 3) & ~3; }
 __device__ __forceinline__ rsrc_t part_rsrc(const DecodeParams& p, int band) {
-  const uint32_t bytes = (uint32_t)p.maxseg * p.T * 64 * 4;
-  return make_rsrc(p.part + (size_t)band * p.maxseg * p.T * 64, bytes);
+  const uint32_t seg = 64u * tokens4(p);  // floats of one partial
+  return make_rsrc(p.part + (size_t)band * p.maxseg * seg, (uint32_t)p.maxseg * seg * 4);
+}
+__device__ __forceinline__ uint32_t part_off(const DecodeParams& p, int sidx, int col, int t) {
+  return (uint32_t)(((sidx * 64 + col) * tokens4(p) + t) * 4);
 }
 
 template <int MT>
@@ -303,39 +348,33 @@ __device__ __forceinline__ void put_part(const DecodeParams& p, int band, int si
                                          const f32x4 (&v)[MT]) {
   const int q = (threadIdx.x & 63) >> 4;
   const rsrc_t r = part_rsrc(p, band);
-  const uint32_t so = (uint32_t)sidx * p.T * 256;
-  for (int mt = 0; mt < MT; ++mt)
-    for (int i = 0; i < 4; ++i) {
-      const int t = 16 * mt + 4 * q + i;
-      if (t < p.T) bstore_dev(r, so + (uint32_t)(t * 64 + col) * 4, 0, v[mt][i]);
-    }
+  for (int mt = 0; mt < MT; ++mt) {
+    const int t = 16 * mt + 4 * q;
+    if (t < p.T) bstore16_dev(r, part_off(p, sidx, col, t), 0, v[mt]);
+  }
 }
 
+// The band's nseg partials summed in segment order; 16 / MT partials are in
+// flight at a time.
 template <int MT>
 __device__ __forceinline__ void sum_parts(const DecodeParams& p, int band, int nseg, int col,
                                           f32x4 (&v)[MT]) {
+  constexpr int CH = 16 / MT;
   const int q = (threadIdx.x & 63) >> 4;
   const rsrc_t r = part_rsrc(p, band);
-  uint32_t off[MT][4];
-  for (int mt = 0; mt < MT; ++mt)
-    for (int i = 0; i < 4; ++i) {
-      const int t = min(16 * mt + 4 * q + i, p.T - 1);
-      off[mt][i] = (uint32_t)(t * 64 + col) * 4;
-      v[mt][i] = 0.f;
-    }
-  // Loads of 8 partials in flight at a time; summed in segment order.
-  const uint32_t seg = (uint32_t)p.T * 256;
-  for (int k0 = 0; k0 < nseg; k0 += 8) {
-    float t[8][MT][4];
-    for (int kk = 0; kk < 8; ++kk) {
-      const uint32_t so = (uint32_t)min(k0 + kk, nseg - 1) * seg;
-      for (int mt = 0; mt < MT; ++mt)
-        for (int i = 0; i < 4; ++i) t[kk][mt][i] = bload_dev(r, off[mt][i], so);
-    }
-    for (int kk = 0; kk < 8; ++kk)
-      if (k0 + kk < nseg)
-        for (int mt = 0; mt < MT; ++mt)
-          for (int i = 0; i < 4; ++i) v[mt][i] += t[kk][mt][i];
+  for (int mt = 0; mt < MT; ++mt) v[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int k0 = 0; k0 < nseg; k0 += CH) {
+    const int n = min(CH, nseg - k0);
+    u32x4 w[CH][MT];
+    for (int kk = 0; kk < CH; ++kk)
+      for (int mt = 0; mt < MT; ++mt) {
+        const int t = 16 * mt + 4 * q;
+        w[kk][mt] = kk < n && t < p.T ? bload16_dev(r, part_off(p, k0 + kk, col, t), 0)
+                                      : u32x4{0u, 0u, 0u, 0u};
+      }
+    for (int kk = 0; kk < CH; ++kk)
+      if (kk < n)
+        for (int mt = 0; mt < MT; ++mt) v[mt] += __builtin_bit_cast(f32x4, w[kk][mt]);
   }
 }
 
@@ -358,7 +397,10 @@ __device__ void finish_rank(const DecodeParams& p, int rb, const f32x4 (&u)[MT])
     }
 }
 
-// Finish a row band (this wave's tile): + alpha * v B^T, then store y.
+// Finish a row band (this wave's tile): + alpha * v B^T, then store y.  The
+// rank loop is split in steps of 32 (at most four for r <= 128); every B
+// fragment and alpha * v word of all steps is requested before the first is
+// used, so the correction costs one memory round trip.
 template <int MT>
 __device__ void finish_row(const DecodeParams& p, int band, f32x4 (&yv)[MT]) {
   const int tid = threadIdx.x, lane = tid & 63, wave = wave_id(), q = lane >> 4, c16 = lane & 15;
@@ -375,33 +417,40 @@ __device__ void finish_row(const DecodeParams& p, int band, f32x4 (&yv)[MT]) {
       }
     }
     __syncthreads();
+    constexpr int kSteps = 4;
+    // Offsets past a buffer's end read as zero: ranks past r contribute
+    // nothing.
+    constexpr uint32_t kOut = 0x80000000u;
     const rsrc_t bs = make_rsrc(p.B, (uint32_t)p.N * p.r * 2);
     const rsrc_t wr = make_rsrc(p.wv32, (uint32_t)p.T * p.r * 4);
     const uint32_t bro = (uint32_t)min(nrow, p.N - 1) * p.r * 2;
-    for (int j0 = 0; j0 < p.r; j0 += 32) {
-      const int jj = j0 + 8 * q;  // this lane's 8 ranks of the K = 32 step
+    u32x4 bfr[kSteps], wv[kSteps][MT][2];
+    for (int k = 0; k < kSteps; ++k) {
+      const int jj = 32 * k + 8 * q;  // this lane's 8 ranks of step k
       const bool jok = jj < p.r;
-      const u32x4 bfr = jok ? bload16(bs, bro + 2 * jj, 0) : u32x4{0, 0, 0, 0};
+      bfr[k] = bload16(bs, jok ? bro + 2 * jj : kOut, 0);
       for (int mt = 0; mt < MT; ++mt) {
         const int t = min(16 * mt + c16, p.T - 1);
-        u32x4 hi = {0, 0, 0, 0}, lo = {0, 0, 0, 0};
-        if (jok) {
-          const uint32_t src = (uint32_t)(t * p.r + jj) * 4;
-          float wv[8];
-          for (int e = 0; e < 8; ++e) wv[e] = bload_dev(wr, src + 4 * e, 0);
-          uint32_t h[8], l[8];
-          for (int e = 0; e < 8; ++e) {
-            const float v = wv[e];
-            h[e] = f32_to_bf16_rne(v);
-            l[e] = f32_to_bf16_rne(v - __uint_as_float(h[e] << 16));
-          }
-          hi = u32x4{h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16),
-                     h[6] | (h[7] << 16)};
-          lo = u32x4{l[0] | (l[1] << 16), l[2] | (l[3] << 16), l[4] | (l[5] << 16),
-                     l[6] | (l[7] << 16)};
+        const uint32_t src = jok ? (uint32_t)(t * p.r + jj) * 4 : kOut;
+        wv[k][mt][0] = bload16_dev(wr, src, 0);
+        wv[k][mt][1] = bload16_dev(wr, src + 16, 0);
+      }
+    }
+    for (int k = 0; k < kSteps; ++k) {
+      if (32 * k >= p.r) break;
+      for (int mt = 0; mt < MT; ++mt) {
+        uint32_t h[8], l[8];
+        for (int e = 0; e < 8; ++e) {
+          const float v = __uint_as_float(wv[k][mt][e >> 2][e & 3]);
+          h[e] = f32_to_bf16_rne(v);
+          l[e] = f32_to_bf16_rne(v - __uint_as_float(h[e] << 16));
         }
-        yv[mt] = mfma16x16x32(hi, bfr, yv[mt]);
-        yv[mt] = mfma16x16x32(lo, bfr, yv[mt]);
+        const u32x4 hi = {h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16),
+                          h[6] | (h[7] << 16)};
+        const u32x4 lo = {l[0] | (l[1] << 16), l[2] | (l[3] << 16), l[4] | (l[5] << 16),
+                          l[6] | (l[7] << 16)};
+        yv[mt] = mfma16x16x32(hi, bfr[k], yv[mt]);
+        yv[mt] = mfma16x16x32(lo, bfr[k], yv[mt]);
       }
     }
   }
