@@ -48,10 +48,31 @@ DecodePlan plan_decode(const Shape& s, int slots) {
   };
   pl.workgroups = wgs(std::min(std::max(slots, 1), kMaxSlots));
   // A band of cost Cb meets at most ceil(Cb * P / cost) + 1 workgroup runs;
-  // the bound grows with P, so the workspace is sized for the largest P.
+  // the bound grows with P, so the workspace is sized for the largest P.  A
+  // row band may take one more partial, the correction.
   const long long pmax = wgs(kMaxSlots);
   const long long cb = (long long)KB * std::max(pl.rank_cost, 1);
-  pl.maxseg = (int)std::min<long long>(pmax, (cb * pmax + pl.cost - 1) / pl.cost + 1);
+  pl.maxseg = (int)std::min<long long>(pmax, (cb * pmax + pl.cost - 1) / pl.cost + 1) +
+              (s.r > 0 ? 1 : 0);
+  // Correction workgroups: those whose runs end within the rank units (the
+  // kernel's unit_begin, evaluated on the host).  They finish their share
+  // early and add alpha v B^T to row bands while the rest still stream, so
+  // those bands' finishers do not wait for the rank bands.
+  // Only worth it when every workgroup streams a long run (its rank work and
+  // the correction then end well before the row bands): at least 32 cost
+  // units per workgroup.
+  pl.correction_wgs = 0;
+  if (s.r > 0 && pl.cost >= 32LL * pl.workgroups) {
+    const long long ru = (long long)pl.rank_bands * KB;
+    const long long rc = (long long)pl.rank_cost * pl.workgroups;
+    auto unit_begin = [&](long long w) {
+      const long long X = w * pl.cost;
+      if (X <= ru * rc) return (X + rc - 1) / rc;
+      return ru + (X - ru * rc + pl.workgroups - 1) / pl.workgroups;
+    };
+    while (pl.correction_wgs < pl.workgroups && unit_begin(pl.correction_wgs + 1) <= ru)
+      ++pl.correction_wgs;
+  }
   return pl;
 }
 

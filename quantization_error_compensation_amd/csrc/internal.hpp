@@ -46,7 +46,10 @@ struct DecodePlan {
   int rank_cost;   // cost of one rank unit (a row unit costs 1)
   long long cost;  // total cost of all units
   int workgroups;  // persistent workgroups, each a run of units of equal cost
-  int maxseg;      // bound on the workgroups sharing one band (any P up to kMaxSlots)
+  int maxseg;      // bound on the partial sums of one band (any P up to kMaxSlots): the
+                   // workgroups sharing it, plus the correction partial when r > 0
+  int correction_wgs;  // the first workgroups, whose runs hold rank units only; they add
+                       // alpha v B^T to the row bands as partials (0: the finishers do)
 };
 
 // Work split of the prefill GEMM: output tiles of kPrefillBM x kPrefillBN,

@@ -67,7 +67,10 @@ struct DecodeParams {
   int P;                   // workgroups
   int rank_cost;           // cost of a rank unit; a row unit costs 1
   long long ctot;          // total cost of all units
-  int maxseg;              // bound on the workgroups sharing one band
+  int maxseg;              // bound on the partial sums of one band
+  int cw;                  // correction workgroups (the first cw, whose runs hold rank
+                           // units only): each adds alpha v B^T to up to
+                           // kCorrBands / MT row bands as one more partial
 };
 
 constexpr int XROW = 272;            // LDS row of one token: 256 B + 16 B pad
@@ -397,63 +400,101 @@ __device__ void finish_rank(const DecodeParams& p, int rb, const f32x4 (&u)[MT])
     }
 }
 
-// Finish a row band (this wave's tile): + alpha * v B^T, then store y.  The
-// rank loop is split in steps of 32 (at most four for r <= 128); every B
-// fragment and alpha * v word of all steps is requested before the first is
-// used, so the correction costs one memory round trip.
+// Row bands whose correction a correction workgroup adds (as an extra
+// partial); kCorrBands / MT bands per correction workgroup.
+constexpr int kCorrBands = 8;
 template <int MT>
-__device__ void finish_row(const DecodeParams& p, int band, f32x4 (&yv)[MT]) {
-  const int tid = threadIdx.x, lane = tid & 63, wave = wave_id(), q = lane >> 4, c16 = lane & 15;
-  const int nrow = band * 64 + 16 * wave + c16;
-  if (p.r > 0) {
-    if (tid == 0) {
-      int spins = 0;
-      while (load_dev(&p.ctr[kCtrRankDone]) < p.RB) {
-        __builtin_amdgcn_s_sleep(2);
-        if (++spins > kSpinLimit) {
-          atomicOr(&p.ctr[kCtrError], 1);
-          break;
-        }
-      }
-    }
-    __syncthreads();
-    constexpr int kSteps = 4;
-    // Offsets past a buffer's end read as zero: ranks past r contribute
-    // nothing.
-    constexpr uint32_t kOut = 0x80000000u;
-    const rsrc_t bs = make_rsrc(p.B, (uint32_t)p.N * p.r * 2);
-    const rsrc_t wr = make_rsrc(p.wv32, (uint32_t)p.T * p.r * 4);
-    const uint32_t bro = (uint32_t)min(nrow, p.N - 1) * p.r * 2;
-    u32x4 bfr[kSteps], wv[kSteps][MT][2];
-    for (int k = 0; k < kSteps; ++k) {
-      const int jj = 32 * k + 8 * q;  // this lane's 8 ranks of step k
-      const bool jok = jj < p.r;
-      bfr[k] = bload16(bs, jok ? bro + 2 * jj : kOut, 0);
-      for (int mt = 0; mt < MT; ++mt) {
-        const int t = min(16 * mt + c16, p.T - 1);
-        const uint32_t src = jok ? (uint32_t)(t * p.r + jj) * 4 : kOut;
-        wv[k][mt][0] = bload16_dev(wr, src, 0);
-        wv[k][mt][1] = bload16_dev(wr, src + 16, 0);
-      }
-    }
-    for (int k = 0; k < kSteps; ++k) {
-      if (32 * k >= p.r) break;
-      for (int mt = 0; mt < MT; ++mt) {
-        uint32_t h[8], l[8];
-        for (int e = 0; e < 8; ++e) {
-          const float v = __uint_as_float(wv[k][mt][e >> 2][e & 3]);
-          h[e] = f32_to_bf16_rne(v);
-          l[e] = f32_to_bf16_rne(v - __uint_as_float(h[e] << 16));
-        }
-        const u32x4 hi = {h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16),
-                          h[6] | (h[7] << 16)};
-        const u32x4 lo = {l[0] | (l[1] << 16), l[2] | (l[3] << 16), l[4] | (l[5] << 16),
-                          l[6] | (l[7] << 16)};
-        yv[mt] = mfma16x16x32(hi, bfr[k], yv[mt]);
-        yv[mt] = mfma16x16x32(lo, bfr[k], yv[mt]);
+__device__ __forceinline__ bool corrected(const DecodeParams& p, int nb) {
+  return nb < p.cw * (kCorrBands / MT);
+}
+
+// Wait (bounded, error word on timeout) until every rank band has published
+// alpha * v.
+__device__ __forceinline__ void wait_ranks(const DecodeParams& p) {
+  if (threadIdx.x == 0) {
+    int spins = 0;
+    while (load_dev(&p.ctr[kCtrRankDone]) < p.RB) {
+      __builtin_amdgcn_s_sleep(1);
+      if (++spins > kSpinLimit) {
+        atomicOr(&p.ctr[kCtrError], 1);
+        break;
       }
     }
   }
+  __syncthreads();
+}
+
+// alpha * v of this lane's tokens as matrix-core operands: for each K = 32
+// rank step k, the bf16 high part and the bf16 remainder of 8 ranks.  Every
+// word of all steps is requested before the first is used.
+constexpr int kRankSteps = 4;  // r <= 128
+template <int MT>
+__device__ __forceinline__ void alpha_v_operands(const DecodeParams& p, u32x4 (&hi)[kRankSteps][MT],
+                                                 u32x4 (&lo)[kRankSteps][MT]) {
+  const int lane = threadIdx.x & 63, q = lane >> 4, c16 = lane & 15;
+  // Offsets past a buffer's end read as zero: ranks past r contribute nothing.
+  constexpr uint32_t kOut = 0x80000000u;
+  const rsrc_t wr = make_rsrc(p.wv32, (uint32_t)p.T * p.r * 4);
+  u32x4 wv[kRankSteps][MT][2];
+  for (int k = 0; k < kRankSteps; ++k) {
+    const int jj = 32 * k + 8 * q;  // this lane's 8 ranks of step k
+    for (int mt = 0; mt < MT; ++mt) {
+      const int t = min(16 * mt + c16, p.T - 1);
+      const uint32_t src = jj < p.r ? (uint32_t)(t * p.r + jj) * 4 : kOut;
+      wv[k][mt][0] = bload16_dev(wr, src, 0);
+      wv[k][mt][1] = bload16_dev(wr, src + 16, 0);
+    }
+  }
+  for (int k = 0; k < kRankSteps; ++k)
+    for (int mt = 0; mt < MT; ++mt) {
+      uint32_t h[8], l[8];
+      for (int e = 0; e < 8; ++e) {
+        const float v = __uint_as_float(wv[k][mt][e >> 2][e & 3]);
+        h[e] = f32_to_bf16_rne(v);
+        l[e] = f32_to_bf16_rne(v - __uint_as_float(h[e] << 16));
+      }
+      hi[k][mt] = u32x4{h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16),
+                        h[6] | (h[7] << 16)};
+      lo[k][mt] = u32x4{l[0] | (l[1] << 16), l[2] | (l[3] << 16), l[4] | (l[5] << 16),
+                        l[6] | (l[7] << 16)};
+    }
+}
+
+// B fragments of the 16 rows of this wave's tile of a row band: for each
+// K = 32 rank step, 8 ranks of the lane's row (zero past r).
+__device__ __forceinline__ void b_fragments(const DecodeParams& p, int band,
+                                            u32x4 (&bfr)[kRankSteps]) {
+  const int lane = threadIdx.x & 63, wave = wave_id(), q = lane >> 4, c16 = lane & 15;
+  const int nrow = band * 64 + 16 * wave + c16;
+  constexpr uint32_t kOut = 0x80000000u;
+  const rsrc_t bs = make_rsrc(p.B, (uint32_t)p.N * p.r * 2);
+  const uint32_t bro = (uint32_t)min(nrow, p.N - 1) * p.r * 2;
+  for (int k = 0; k < kRankSteps; ++k) {
+    const int jj = 32 * k + 8 * q;
+    bfr[k] = bload16(bs, jj < p.r ? bro + 2 * jj : kOut, 0);
+  }
+}
+
+// yv += alpha * v B^T for the 16 rows of this wave's tile of a row band, as
+// K = r matrix-core products (v split into bf16 high and low parts).
+template <int MT>
+__device__ __forceinline__ void add_correction(const DecodeParams& p, const u32x4 (&bfr)[kRankSteps],
+                                               const u32x4 (&hi)[kRankSteps][MT],
+                                               const u32x4 (&lo)[kRankSteps][MT], f32x4 (&yv)[MT]) {
+  for (int k = 0; k < kRankSteps; ++k) {
+    if (32 * k >= p.r) break;
+    for (int mt = 0; mt < MT; ++mt) {
+      yv[mt] = mfma16x16x32(hi[k][mt], bfr[k], yv[mt]);
+      yv[mt] = mfma16x16x32(lo[k][mt], bfr[k], yv[mt]);
+    }
+  }
+}
+
+// Store y for this wave's tile of a finished row band.
+template <int MT>
+__device__ __forceinline__ void store_row(const DecodeParams& p, int band, const f32x4 (&yv)[MT]) {
+  const int lane = threadIdx.x & 63, wave = wave_id(), q = lane >> 4, c16 = lane & 15;
+  const int nrow = band * 64 + 16 * wave + c16;
   if (nrow < p.N)
     for (int mt = 0; mt < MT; ++mt)
       for (int i = 0; i < 4; ++i) {
@@ -462,12 +503,94 @@ __device__ void finish_row(const DecodeParams& p, int band, f32x4 (&yv)[MT]) {
       }
 }
 
+// Add a partial sum to a band (slot sidx of nparts) and report whether this
+// workgroup arrived last; the last one gets the sum of all partials in slot
+// order in v and clears the band's counter.
+template <int MT>
+__device__ __forceinline__ bool arrive(const DecodeParams& p, int band, int sidx, int nparts,
+                                       int* s_last, f32x4 (&v)[MT]) {
+  const int tid = threadIdx.x, col = 16 * wave_id() + (tid & 15);
+  put_part<MT>(p, band, sidx, col, v);
+  wait_vmem();
+  __syncthreads();
+  if (tid == 0) *s_last = atomicAdd(&p.ctr[kCtrBand + band], 1) == nparts - 1;
+  __syncthreads();
+  const bool last = *s_last;
+  if (last) {
+    sum_parts<MT>(p, band, nparts, col, v);
+    if (tid == 0) store_dev(&p.ctr[kCtrBand + band], 0);
+  }
+  return last;
+}
+
+// The correction workgroups: once the rank bands are published, alpha v B^T
+// of row bands wg, wg + cw, ... (kCorrBands / MT of them) goes in as each
+// band's extra partial (slot nseg); whoever arrives last at a band stores it.
+// All their B fragments are requested together, their partials stored
+// together, and one wait covers all the stores.  The finishers of the bands
+// from cw * kCorrBands / MT on add the correction themselves.
+template <int MT>
+__device__ void correction_partials(const DecodeParams& p, int wg, int* s_mask) {
+  constexpr int kCorrBatch = kCorrBands / MT;
+  const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
+  const int col = 16 * wave + (lane & 15);
+  // B does not depend on the rank bands: its fragments are requested first.
+  u32x4 bfr[kCorrBatch][kRankSteps];
+  for (int i = 0; i < kCorrBatch; ++i) b_fragments(p, min(wg + i * p.cw, p.NB - 1), bfr[i]);
+  wait_ranks(p);
+  u32x4 hi[kRankSteps][MT], lo[kRankSteps][MT];
+  alpha_v_operands<MT>(p, hi, lo);
+  {
+    const int nb0 = wg;
+    int nseg[kCorrBatch];
+    bool ok[kCorrBatch];
+    f32x4 v[kCorrBatch][MT];
+    for (int i = 0; i < kCorrBatch; ++i) {
+      const int nb = nb0 + i * p.cw, band = p.RB + nb;
+      const long long bbeg = (long long)band * p.KB, bend = bbeg + p.KB;
+      ok[i] = nb < p.NB;
+      nseg[i] = ok[i] ? owner_of(p, bend - 1) - owner_of(p, bbeg) + 1 : 0;
+      if (ok[i] && nseg[i] + 1 > p.maxseg) {  // cannot happen with a planner-sized workspace
+        if (tid == 0) atomicOr(&p.ctr[kCtrError], 2);
+        ok[i] = false;
+      }
+      for (int mt = 0; mt < MT; ++mt) v[i][mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+      if (ok[i]) add_correction<MT>(p, bfr[i], hi, lo, v[i]);
+    }
+    for (int i = 0; i < kCorrBatch; ++i)
+      if (ok[i]) put_part<MT>(p, p.RB + nb0 + i * p.cw, nseg[i], col, v[i]);
+    wait_vmem();
+    __syncthreads();
+    if (wave == 0) {  // lane i counts band i in; the arrivals go out together
+      bool last = false;
+      if (lane < kCorrBatch) {
+        const int nb = nb0 + lane * p.cw, band = p.RB + nb;
+        const long long bbeg = (long long)band * p.KB, bend = bbeg + p.KB;
+        const int ns = nb < p.NB ? owner_of(p, bend - 1) - owner_of(p, bbeg) + 1 : 0;
+        if (nb < p.NB && ns + 1 <= p.maxseg)
+          last = atomicAdd(&p.ctr[kCtrBand + band], 1) == ns;
+      }
+      const uint64_t m = __ballot(last);
+      if (lane == 0) *s_mask = (int)(m & ((1u << kCorrBatch) - 1));
+    }
+    __syncthreads();
+    const int mask = *s_mask;
+    for (int i = 0; i < kCorrBatch; ++i)
+      if (mask & (1 << i)) {  // arrived last: every segment's partial is in
+        const int nb = nb0 + i * p.cw, band = p.RB + nb;
+        sum_parts<MT>(p, band, nseg[i] + 1, col, v[i]);
+        if (tid == 0) store_dev(&p.ctr[kCtrBand + band], 0);
+        store_row<MT>(p, nb, v[i]);
+      }
+  }
+}
+
 template <int MT, bool GROUPED>
 __global__ __launch_bounds__(256, 2) void decode_kernel(DecodeParams p) {
   __shared__ __attribute__((aligned(16))) uint8_t xlds[2 * Burst<MT>::kBuf];
   __shared__ __attribute__((aligned(16))) uint8_t mlds[GROUPED ? 4 * kMetaWave : 16];
   __shared__ int s_last;
-  const int tid = threadIdx.x, lane = tid & 63, wave = wave_id(), c16 = lane & 15;
+  const int tid = threadIdx.x;
   const int wg = blockIdx.x;
   const long long u0 = unit_begin(p, wg), u1 = unit_begin(p, wg + 1);
   int burst = 0;
@@ -482,7 +605,11 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(DecodeParams p) {
     const int nseg = owner_of(p, bend - 1) - first + 1;
     const int sidx = wg - first;
     const bool rank = band < p.RB;
-    if (nseg > p.maxseg) {  // cannot happen with a workspace sized by the planner
+    // a row band whose correction a correction workgroup adds takes one more
+    // partial
+    const bool corr = !rank && corrected<MT>(p, band - p.RB);
+    const int nparts = nseg + (corr ? 1 : 0);
+    if (nparts > p.maxseg) {  // cannot happen with a workspace sized by the planner
       if (tid == 0) atomicOr(&p.ctr[kCtrError], 2);
       continue;
     }
@@ -490,21 +617,8 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(DecodeParams p) {
     f32x4 v[MT];
     if (rank) rank_segment<MT>(p, band, lo, hi, xlds, burst, v);
     else row_segment<MT, GROUPED>(p, band - p.RB, lo, hi, xlds, mlds, burst, v);
-    const int col = 16 * wave + c16;
 
-    bool fin = nseg == 1;
-    if (!fin) {
-      put_part<MT>(p, band, sidx, col, v);
-      wait_vmem();
-      __syncthreads();
-      if (tid == 0) s_last = atomicAdd(&p.ctr[kCtrBand + band], 1) == nseg - 1;
-      __syncthreads();
-      fin = s_last;
-      if (fin) {
-        sum_parts<MT>(p, band, nseg, col, v);
-        if (tid == 0) store_dev(&p.ctr[kCtrBand + band], 0);
-      }
-    }
+    const bool fin = nparts == 1 || arrive<MT>(p, band, sidx, nparts, &s_last, v);
     if (fin) {
       if (rank) {
         finish_rank<MT>(p, band, v);
@@ -512,10 +626,19 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(DecodeParams p) {
         __syncthreads();
         if (tid == 0) atomicAdd(&p.ctr[kCtrRankDone], 1);
       } else {
-        finish_row<MT>(p, band - p.RB, v);
+        if (p.r > 0 && !corr) {
+          u32x4 bfr[kRankSteps];
+          b_fragments(p, band - p.RB, bfr);
+          wait_ranks(p);
+          u32x4 vhi[kRankSteps][MT], vlo[kRankSteps][MT];
+          alpha_v_operands<MT>(p, vhi, vlo);
+          add_correction<MT>(p, bfr, vhi, vlo, v);
+        }
+        store_row<MT>(p, band - p.RB, v);
       }
     }
   }
+  if (wg < p.cw) correction_partials<MT>(p, wg, &s_last);
 
   if (p.RB > 0 && tid == 0) {
     wait_vmem();
@@ -579,6 +702,7 @@ hipError_t launch_decode(const Shape& s, const LayerArgs& a, const WsPtrs& w, hi
   p.rank_cost = pl.rank_cost;
   p.ctot = pl.cost;
   p.maxseg = pl.maxseg;
+  p.cw = pl.correction_wgs;
   if (s.T <= 16) return s.grouped ? go<1, true>(p, st) : go<1, false>(p, st);
   return s.grouped ? go<2, true>(p, st) : go<2, false>(p, st);
 }
