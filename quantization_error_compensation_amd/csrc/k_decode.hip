@@ -18,7 +18,7 @@
 //
 // Inside a segment the four waves of a workgroup own one 16-row tile each
 // and walk the same K blocks in bursts of NS blocks:
-//   * in row bands every load of a burst (x, codes, metadata) is issued one
+//   * every load of a burst (x, codes or A rows, metadata) is issued one
 //     burst ahead, into registers, so it is in flight while the previous
 //     burst computes;
 //   * x of the burst is loaded once per workgroup (each wave 4 tokens x
@@ -152,7 +152,23 @@ __device__ __forceinline__ void x_frags(const uint8_t* buf, int i, int lane, u32
 }
 
 // ------------------------------------------------------------ rank segment
+// A barrier that leaves global loads in flight: only this wave's LDS writes
+// are awaited before the workgroup meets.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// What one burst of a rank segment takes from memory: x and the A rows.
+template <int MT, int NS>
+struct RankStage {
+  XStage<MT, NS> x;
+  u32x4 a[NS][4];
+};
+
 // Ranks 64 rb + 16 wave + c16, blocks [lo, hi): u = x A^T over the segment.
+// Loads run one burst ahead, in two register stages, as in row segments.
 template <int MT>
 __device__ void rank_segment(const DecodeParams& p, int rb, int lo, int hi, uint8_t* xlds,
                              int& burst, f32x4 (&uo)[MT]) {
@@ -162,31 +178,45 @@ __device__ void rank_segment(const DecodeParams& p, int rb, int lo, int hi, uint
   // (its u columns are never published)
   const int j0 = min(64 * rb + 16 * wave, p.r - 16);
   const uint32_t arowB = (uint32_t)p.K * 2;
-  const uint16_t* At = p.A + (size_t)j0 * p.K;
+  const rsrc_t ar = make_rsrc(p.A + (size_t)j0 * p.K, 16u * arowB);
   const uint32_t ao = (uint32_t)c16 * arowB + 64u * q;  // pieces 4q .. 4q + 3 of row c16
   for (int mt = 0; mt < MT; ++mt) uo[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  for (int b = lo; b < hi; b += NS, ++burst) {
-    uint8_t* buf = xlds + (burst & 1) * Burst<MT>::kBuf;
-    XStage<MT, NS> xsg;
-    x_issue<MT, NS>(p, wave, lane, b, hi, true, xsg);
-    u32x4 a[NS][4];
+  auto issue = [&](RankStage<MT, NS>& s, int b) {
+    const bool live = b < hi;  // a burst past the segment loads nothing
+    x_issue<MT, NS>(p, wave, lane, b, hi, live, s.x);
+    const uint32_t av = live ? ao : 0x80000000u;
     for (int i = 0; i < NS; ++i)
       for (int j = 0; j < 4; ++j)
-        a[i][j] = gload16(At, ao + 16 * j + (uint32_t)min(b + i, hi - 1) * 256);
-    x_store<MT, NS>(buf, wave, lane, xsg);
-    __syncthreads();
+        s.a[i][j] = bload16(ar, av + 16 * j, (uint32_t)min(b + i, hi - 1) * 256);
+  };
+  auto consume = [&](RankStage<MT, NS>& s, int b) {
+    uint8_t* buf = xlds + (burst & 1) * Burst<MT>::kBuf;
+    ++burst;
+    x_store<MT, NS>(buf, wave, lane, s.x);
+    lds_barrier();
 #pragma unroll
     for (int i = 0; i < NS; ++i) {
       if (b + i < hi) {
         u32x4 xf[MT][4];
         x_frags<MT>(buf, i, lane, xf);
         for (int j = 0; j < 4; ++j) {
-          const u32x4 ap = x_permute8(a[i][j]);
+          const u32x4 ap = x_permute8(s.a[i][j]);
           for (int mt = 0; mt < MT; ++mt) uo[mt] = mfma16x16x32(xf[mt][j], ap, uo[mt]);
         }
       }
     }
+  };
+
+  RankStage<MT, NS> s0, s1;
+  issue(s0, lo);
+  for (int b = lo;; b += 2 * NS) {
+    issue(s1, b + NS);
+    consume(s0, b);
+    if (b + NS >= hi) break;
+    issue(s0, b + 2 * NS);
+    consume(s1, b + NS);
+    if (b + 2 * NS >= hi) break;
   }
 }
 
@@ -210,14 +240,6 @@ struct RowStage {
   u32x4 w[NS];
   uint32_t sv[8], zv[2];
 };
-
-// A barrier that leaves global loads in flight: only this wave's LDS writes
-// are awaited before the workgroup meets.
-__device__ __forceinline__ void lds_barrier() {
-  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-  __builtin_amdgcn_s_barrier();
-  asm volatile("" ::: "memory");
-}
 
 // Rows 64 band + 16 wave + c16 (this wave's tile), blocks [lo, hi): partial
 // y with the scales applied.
