@@ -81,6 +81,9 @@ WORKLOADS = {
     "c4": dict(steps=[("decode", 1), ("decode", 16), ("prefill", 256), ("prefill", 4096)],
                text="d_in=d_out=8192 sweep point, int4 symmetric per-channel, rank 128; tokens "
                     "1, 16, 256, 4096"),
+    "v1": dict(steps=[("decode", 9)],
+               text="Quasar-shaped verify pass: d_in=d_out=8192, int4 symmetric per-tensor, no "
+                    "compensator (rank 0); 9 tokens (8 drafted + 1)"),
 }
 
 
@@ -137,7 +140,7 @@ def main():
     W = synth.weights(spec)
     X = synth.activations(spec, Ttot)
     A, B, gv, bv = synth.compensator(spec, r)
-    desc = q.make_desc(K, N, r, g, asym)
+    desc = q.make_desc(K, N, r, g, asym, spec.per_tensor)
     wq0, sc0, zs0 = q.alloc_packed(desc, dev)
     q.spear_ec_quantize_rtn(desc, to_dev_f32(W, dev), wq0, sc0, zs0)
     torch.cuda.synchronize()
@@ -233,7 +236,8 @@ def main():
         "dtype": "bf16", "data": "synthetic",
         "config": {"workload": f"{args.config}: " + WORKLOADS[args.config]["text"],
                    "d_in": K, "d_out": N, "rank": r, "group_size": g,
-                   "zero_points": asym, "tokens_per_step": [T for _, T in plan],
+                   "zero_points": asym, "per_tensor": spec.per_tensor,
+                   "tokens_per_step": [T for _, T in plan],
                    "weight_copies_rotated": copies, "parallelism": "single GPU"},
         "calls": [{k: (round(v, 4) if isinstance(v, float) else v) for k, v in c.items()}
                   for c in calls],
@@ -335,7 +339,7 @@ def cpu_baseline(spec, r, plan, X, A, B, gv, bv, unit):
     import synth
     Wsl = synth.weights(spec, rows=rows)
     t0 = time.time()
-    wq, sc, zs = oracle.quantize_rtn(Wsl, g, asym)
+    wq, sc, zs = oracle.quantize_rtn_per_tensor(Wsl) if spec.per_tensor else oracle.quantize_rtn(Wsl, g, asym)
     t1 = time.time()
     oracle.forward(x, wq, sc, zs, A if r else None, B[:rows] if r else None, gv, bv, spec.alpha, g)
     t2 = time.time()

@@ -64,7 +64,8 @@ extern "C" {
 #define SPEAR_EC_ERR_HIP 5              /* HIP launch / runtime error (see last_error)     */
 
 /* desc.flags */
-#define SPEAR_EC_ZEROS 1 /* asymmetric codes: `zeros` is present and required */
+#define SPEAR_EC_ZEROS 1      /* asymmetric codes: `zeros` is present and required */
+#define SPEAR_EC_PER_TENSOR 2 /* one symmetric scale for the whole tensor (stored per row) */
 
 /* Largest token count the decode path accepts (decode = 1..32 tokens). */
 #define SPEAR_EC_DECODE_MAX_TOKENS 32
@@ -75,7 +76,11 @@ extern "C" {
  *   d_out      multiple of 16, 16 .. 131072
  *   rank       0 (plain W4, no compensator) or a multiple of 16 up to 128
  *   group_size d_in (per-output-channel scales) or 128
- *   flags      0 or SPEAR_EC_ZEROS
+ *   flags      0, SPEAR_EC_ZEROS, or SPEAR_EC_PER_TENSOR (with group_size ==
+ *              d_in and no zeros: the symmetric per-tensor format of the
+ *              Quasar verify pass, summary "Targeted quantization"; it is
+ *              stored as per-channel scales that are all equal, so the layer
+ *              calls treat it as per-channel and only the quantizer differs)
  * Passed by pointer and read during the call only.
  */
 typedef struct spear_ec_desc {
@@ -146,6 +151,8 @@ int spear_ec_linear_prefill(const spear_ec_desc* desc, int32_t tokens, const voi
  * codes clamp(rint(W/s) + z, 0, 15).  Ratios are formed in double, rint rounds
  * half to even, a scale that rounds to 0 becomes 1, and fp16 rounding of a
  * scale saturates at 65504.  `zeros` is written only with SPEAR_EC_ZEROS.
+ * With SPEAR_EC_PER_TENSOR one scale s = RN_fp16(max|W| / 7) over the whole
+ * tensor (written to every row's scale), codes as in the symmetric case.
  * desc.rank is ignored.
  */
 int spear_ec_quantize_rtn(const spear_ec_desc* desc, const float* w, uint32_t* wq,

@@ -54,6 +54,8 @@ def _load():
         lib.orc_sigmoid.restype = ctypes.c_double
         lib.orc_quantize_rtn.argtypes = [P, i32, i32, i32, i32, P, P, P]
         lib.orc_quantize_rtn.restype = i32
+        lib.orc_quantize_rtn_per_tensor.argtypes = [P, i32, i32, P, P]
+        lib.orc_quantize_rtn_per_tensor.restype = i32
         lib.orc_code.argtypes = [P, i32, i32, i32]
         lib.orc_code.restype = i32
         lib.orc_zero.argtypes = [P, i32, i32, i32]
@@ -120,6 +122,19 @@ def quantize_rtn(W: np.ndarray, group_size: int, asym: bool):
     if rc != 0:
         raise ValueError("oracle quantizer rejected the shape")
     return wq, sc, zs
+
+
+def quantize_rtn_per_tensor(W: np.ndarray):
+    """Symmetric per-tensor RTN int4 quantization + packing (Quasar summary,
+    "Targeted quantization"). Returns (wq uint32 [N][K/8], scales uint16 [N][1],
+    all equal, None)."""
+    W = _c(W, np.float32)
+    N, K = W.shape
+    wq = np.zeros((N, K // 8), np.uint32)
+    sc = np.zeros((N, 1), np.uint16)
+    if _load().orc_quantize_rtn_per_tensor(_p(W), N, K, _p(wq), _p(sc)) != 0:
+        raise ValueError("oracle quantizer rejected the shape")
+    return wq, sc, None
 
 
 def codes(wq: np.ndarray, K: int) -> np.ndarray:

@@ -13,7 +13,9 @@
 //
 //   * RTN int4 weight quantization (SPEAR summary, section 3.1, quality
 //     recovery: the hard setting is RTN with per-channel scales). Symmetric
-//     per-output-channel and asymmetric group-wise with zero-points.
+//     per-output-channel and asymmetric group-wise with zero-points; and the
+//     symmetric per-tensor scale of the Quasar verify pass (Quasar summary,
+//     "Targeted quantization": one symmetric scaling factor per tensor).
 //   * Unpack / dequantization of the packed codes:  W~[n,k] = (c - z) * s.
 //   * The compensated product (SPEAR summary, section 2.1 A, input-adaptive
 //     error compensators): the effective weight for token x is
@@ -175,6 +177,29 @@ int orc_quantize_rtn(const float* W, int N, int K, int g, int asym,
         const int k = j * g + kk;
         wq[(size_t)n * (K / 8) + k / 8] |= (uint32_t)codes[kk] << (4 * (k % 8));
       }
+    }
+  }
+  return 0;
+}
+
+// Symmetric per-tensor RTN: one scale s = RN_fp16(max over all of W of |w| / 7)
+// (1 if it rounds to 0), codes clamp(rint(w/s), -8, 7) + 8, packed as above.
+// The stored format is the per-channel one with every row's scale set to s.
+// Returns 0, or -1 on a shape it does not accept.
+int orc_quantize_rtn_per_tensor(const float* W, int N, int K, uint32_t* wq, uint16_t* scales) {
+  if (N < 0 || K <= 0 || K % 8 != 0) return -1;
+  double m = 0.0;
+  for (size_t i = 0; i < (size_t)N * K; ++i) m = std::max(m, std::fabs((double)W[i]));
+  uint16_t sb = orc_double_to_half(m / 7.0);
+  if (orc_half_to_double(sb) == 0.0) sb = 0x3C00;
+  const double s = orc_half_to_double(sb);
+  std::memset(wq, 0, sizeof(uint32_t) * (size_t)N * (K / 8));
+  for (int n = 0; n < N; ++n) {
+    scales[n] = sb;
+    for (int k = 0; k < K; ++k) {
+      double q = std::nearbyint((double)W[(size_t)n * K + k] / s);
+      q = std::min(7.0, std::max(-8.0, q));
+      wq[(size_t)n * (K / 8) + k / 8] |= (uint32_t)(q + 8.0) << (4 * (k % 8));
     }
   }
   return 0;

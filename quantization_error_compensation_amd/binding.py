@@ -22,6 +22,7 @@ SPEAR_EC_ERR_MISALIGNED = 3
 SPEAR_EC_ERR_WORKSPACE = 4
 SPEAR_EC_ERR_HIP = 5
 SPEAR_EC_ZEROS = 1
+SPEAR_EC_PER_TENSOR = 2
 SPEAR_EC_DECODE_MAX_TOKENS = 32
 
 EXPORTED = (
@@ -76,8 +77,10 @@ def load_library(path: str = LIB_PATH):
     return lib
 
 
-def make_desc(d_in: int, d_out: int, rank: int, group_size: int, zeros: bool) -> spear_ec_desc:
-    return spear_ec_desc(d_in, d_out, rank, group_size, SPEAR_EC_ZEROS if zeros else 0)
+def make_desc(d_in: int, d_out: int, rank: int, group_size: int, zeros: bool,
+              per_tensor: bool = False) -> spear_ec_desc:
+    flags = (SPEAR_EC_ZEROS if zeros else 0) | (SPEAR_EC_PER_TENSOR if per_tensor else 0)
+    return spear_ec_desc(d_in, d_out, rank, group_size, flags)
 
 
 def _ptr(t):

@@ -159,7 +159,10 @@ static int check_desc(const spear_ec_desc* d, bool need_rank) {
   if (!d) return fail(SPEAR_EC_ERR_INVALID_ARGUMENT, "desc is NULL");
   if (d->d_in <= 0 || d->d_out <= 0 || d->rank < 0 || d->group_size <= 0)
     return fail(SPEAR_EC_ERR_INVALID_ARGUMENT, "desc has a non-positive size");
-  if (d->flags & ~SPEAR_EC_ZEROS) return fail(SPEAR_EC_ERR_INVALID_ARGUMENT, "unknown desc.flags bits");
+  if (d->flags & ~(SPEAR_EC_ZEROS | SPEAR_EC_PER_TENSOR))
+    return fail(SPEAR_EC_ERR_INVALID_ARGUMENT, "unknown desc.flags bits");
+  if ((d->flags & SPEAR_EC_PER_TENSOR) && ((d->flags & SPEAR_EC_ZEROS) || d->group_size != d->d_in))
+    return fail(SPEAR_EC_ERR_UNSUPPORTED, "SPEAR_EC_PER_TENSOR needs group_size == d_in and no zeros");
   if (d->d_in % 128 != 0 || d->d_in > 131072)
     return fail(SPEAR_EC_ERR_UNSUPPORTED, "d_in must be a multiple of 128 and at most 131072");
   if (d->d_out % 16 != 0 || d->d_out > 131072)
@@ -294,7 +297,8 @@ int spear_ec_quantize_rtn(const spear_ec_desc* desc, const float* w, uint32_t* w
     return fail(SPEAR_EC_ERR_INVALID_ARGUMENT, "w, wq, scales (and zeros when asymmetric) are required");
   if (!aligned16(w) || !aligned16(wq) || !aligned16(scales) || (asym && !aligned16(zeros)))
     return fail(SPEAR_EC_ERR_MISALIGNED, "a pointer is not 16-byte aligned");
-  return hip_status(launch_quantize(desc->d_out, desc->d_in, desc->group_size, asym, w, wq,
+  return hip_status(launch_quantize(desc->d_out, desc->d_in, desc->group_size, asym,
+                                    (desc->flags & SPEAR_EC_PER_TENSOR) != 0, w, wq,
                                     static_cast<uint16_t*>(scales), asym ? zeros : nullptr, stream),
                     "quantize kernel launch");
 }

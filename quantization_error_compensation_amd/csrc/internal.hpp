@@ -101,8 +101,8 @@ hipError_t launch_projection(const Shape& s, const LayerArgs& a, const WsPtrs& w
                              hipStream_t st);
 hipError_t launch_decode(const Shape& s, const LayerArgs& a, const WsPtrs& w, hipStream_t st);
 hipError_t launch_prefill(const Shape& s, const LayerArgs& a, const WsPtrs& w, hipStream_t st);
-hipError_t launch_quantize(int N, int K, int g, bool asym, const float* w, uint32_t* wq,
-                           uint16_t* scales, uint32_t* zeros, hipStream_t st);
+hipError_t launch_quantize(int N, int K, int g, bool asym, bool per_tensor, const float* w,
+                           uint32_t* wq, uint16_t* scales, uint32_t* zeros, hipStream_t st);
 hipError_t launch_dequant(int N, int K, int g, const uint32_t* wq, const uint16_t* scales,
                           const uint32_t* zeros, float* out, hipStream_t st);
 

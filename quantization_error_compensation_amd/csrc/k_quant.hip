@@ -48,11 +48,17 @@ __device__ __forceinline__ float wave_min(float v) {
 }
 
 // One workgroup (4 waves) per output row; wave w handles groups w, w+4, ...
+// mode kGroups: scale and codes of every group.  Per-tensor scales take two
+// more passes: kRowScale writes each row's RN_fp16(max|W| / 7) (no codes;
+// rounding is monotonic, so the largest of them is the tensor's), and after
+// scale_max_kernel has set every row to that scale, kGivenScale writes the
+// codes for the row's stored scale.
+enum QuantMode { kGroups = 0, kRowScale = 1, kGivenScale = 2 };
 __global__ __launch_bounds__(256) void quantize_rtn_kernel(const float* __restrict__ w,
                                                            uint32_t* __restrict__ wq,
                                                            uint16_t* __restrict__ scales,
                                                            uint32_t* __restrict__ zeros, int K,
-                                                           int g, int asym) {
+                                                           int g, int asym, int mode) {
   __shared__ uint8_t zb[1024];
   const int n = blockIdx.x;
   const int lane = threadIdx.x & 63, wave = wave_id();
@@ -74,12 +80,18 @@ __global__ __launch_bounds__(256) void quantize_rtn_kernel(const float* __restri
     double s;
     uint16_t sb;
     double z = 8.0;
-    if (!asym) {
+    if (mode == kGivenScale) {
+      sb = scales[(size_t)n * G + j];
+    } else if (!asym) {
       sb = f64_to_f16_rne_sat((double)wave_max(am) / 7.0);
     } else {
       lo = wave_min(lo);
       hi = wave_max(hi);
       sb = f64_to_f16_rne_sat(((double)hi - (double)lo) / 15.0);
+    }
+    if (mode == kRowScale) {  // the raw rounded scale, 0 kept
+      if (lane == 0) scales[(size_t)n * G + j] = sb;
+      continue;
     }
     if ((sb & 0x7FFFu) == 0) sb = 0x3C00u;
     s = f16_bits_to_f64(sb);
@@ -113,6 +125,20 @@ __global__ __launch_bounds__(256) void quantize_rtn_kernel(const float* __restri
   }
 }
 
+// One workgroup: the largest of the N row scales (positive fp16 bits order
+// like their values), 1.0 if it is 0, written back to every row.
+__global__ __launch_bounds__(256) void scale_max_kernel(uint16_t* __restrict__ scales, int N) {
+  __shared__ uint32_t part[4];
+  uint32_t m = 0;
+  for (int n = threadIdx.x; n < N; n += 256) m = max(m, (uint32_t)scales[n]);
+  for (int o = 32; o > 0; o >>= 1) m = max(m, (uint32_t)__shfl_xor((int)m, o, 64));
+  if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = m;
+  __syncthreads();
+  m = max(max(part[0], part[1]), max(part[2], part[3]));
+  const uint16_t sb = (m & 0x7FFFu) == 0 ? (uint16_t)0x3C00u : (uint16_t)m;
+  for (int n = threadIdx.x; n < N; n += 256) scales[n] = sb;
+}
+
 // One thread per packed word: eight fp32 outputs (c - z) * s, exact.
 __global__ __launch_bounds__(256) void dequant_kernel(const uint32_t* __restrict__ wq,
                                                       const uint16_t* __restrict__ scales,
@@ -137,11 +163,20 @@ __global__ __launch_bounds__(256) void dequant_kernel(const uint32_t* __restrict
 
 }  // namespace
 
-hipError_t launch_quantize(int N, int K, int g, bool asym, const float* w, uint32_t* wq,
-                           uint16_t* scales, uint32_t* zeros, hipStream_t st) {
+hipError_t launch_quantize(int N, int K, int g, bool asym, bool per_tensor, const float* w,
+                           uint32_t* wq, uint16_t* scales, uint32_t* zeros, hipStream_t st) {
   if (N == 0) return hipSuccess;
-  hipLaunchKernelGGL(quantize_rtn_kernel, dim3(N), dim3(256), 0, st, w, wq, scales, zeros, K, g,
-                     asym ? 1 : 0);
+  if (!per_tensor) {
+    hipLaunchKernelGGL(quantize_rtn_kernel, dim3(N), dim3(256), 0, st, w, wq, scales, zeros, K, g,
+                       asym ? 1 : 0, (int)kGroups);
+    return hipGetLastError();
+  }
+  // per-tensor: symmetric, g == K (one scale per row in the stored format)
+  hipLaunchKernelGGL(quantize_rtn_kernel, dim3(N), dim3(256), 0, st, w, wq, scales, zeros, K, K,
+                     0, (int)kRowScale);
+  hipLaunchKernelGGL(scale_max_kernel, dim3(1), dim3(256), 0, st, scales, N);
+  hipLaunchKernelGGL(quantize_rtn_kernel, dim3(N), dim3(256), 0, st, w, wq, scales, zeros, K, K,
+                     0, (int)kGivenScale);
   return hipGetLastError();
 }
 

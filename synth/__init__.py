@@ -48,6 +48,7 @@ class LayerSpec:
     alpha: float = 1.0
     seed_base: int = 0         # 1000 * config index
     tokens: tuple = field(default=(4,))
+    per_tensor: bool = False   # one symmetric scale for the whole tensor
 
 
 CONFIGS = {
@@ -57,6 +58,11 @@ CONFIGS = {
                     seed_base=2000, tokens=(2048,)),
     "c3": LayerSpec(28672, 8192, 64, 128, True, w_std=0.01, seed_base=3000, tokens=(512, 16)),
     "c4": LayerSpec(8192, 8192, 128, 8192, False, seed_base=4000, tokens=(1, 16, 256, 4096)),
+    # Quasar-shaped verify pass (Quasar summary, "Targeted quantization"):
+    # symmetric per-tensor int4, no compensator, draft length + 1 tokens; the
+    # layer shape and value distributions are those of c4.
+    "v1": LayerSpec(8192, 8192, 0, 8192, False, seed_base=5000, tokens=(2, 5, 9),
+                    per_tensor=True),
 }
 C4_RANKS = (0, 16, 64, 128)
 

@@ -76,6 +76,10 @@ def test_validation_codes(lib, name):
     assert _call(lib, name, good, 4, {**FAKE, "A": None}) == binding.SPEAR_EC_ERR_INVALID_ARGUMENT
     assert _call(lib, name, good, 4, {**FAKE, "x": FAKE["x"] + 2}) == binding.SPEAR_EC_ERR_MISALIGNED
     assert _call(lib, name, good, 4, {**FAKE, "ws": None}) == binding.SPEAR_EC_ERR_WORKSPACE
+    # per-tensor scales: symmetric and per-channel layout only
+    for bad in [q.make_desc(512, 512, 16, 512, True, True), q.make_desc(512, 512, 16, 128, False, True)]:
+        assert _call(lib, name, bad, 4, FAKE) == binding.SPEAR_EC_ERR_UNSUPPORTED
+    assert _call(lib, name, q.make_desc(512, 512, 16, 512, False, True), 0) == binding.SPEAR_EC_OK
     assert _call(lib, name, good, 4, FAKE, ws_bytes=64) == binding.SPEAR_EC_ERR_WORKSPACE
     assert q.spear_ec_last_error()
     # rank 0: compensator pointers may be NULL (still stopped by the small workspace)

@@ -65,8 +65,11 @@ class FullLayer:
         self.K, self.N, self.g, self.asym = spec.d_in, spec.d_out, spec.group_size, spec.asym
         note(f"{name}: weights {self.N}x{self.K}, g={self.g}, asym={self.asym}")
         W = synth.weights(spec)
-        self.o_wq, self.o_sc, self.o_zs = oracle.quantize_rtn(W, self.g, self.asym)
-        d = q.make_desc(self.K, self.N, 0, self.g, self.asym)
+        if spec.per_tensor:
+            self.o_wq, self.o_sc, self.o_zs = oracle.quantize_rtn_per_tensor(W)
+        else:
+            self.o_wq, self.o_sc, self.o_zs = oracle.quantize_rtn(W, self.g, self.asym)
+        d = q.make_desc(self.K, self.N, 0, self.g, self.asym, spec.per_tensor)
         self.d_wq, self.d_sc, self.d_zs = q.alloc_packed(d)
         note(f"{name}: GPU quantize")
         q.spear_ec_quantize_rtn(d, to_dev_f32(W), self.d_wq, self.d_sc, self.d_zs)
@@ -85,7 +88,7 @@ class FullLayer:
         spec = self.spec
         x = synth.activations(spec, T)
         A, B, gv, bv = synth.compensator(spec, r)
-        desc = q.make_desc(self.K, self.N, r, self.g, self.asym)
+        desc = q.make_desc(self.K, self.N, r, self.g, self.asym, spec.per_tensor)
         y = torch.empty((T, self.N), dtype=torch.bfloat16, device="cuda")
         ws = q.alloc_workspace(desc, T)
         dev = (to_dev_bf16(A), to_dev_bf16(B), to_dev_f32(gv), to_dev_f32(bv)) if r else (None,) * 4
@@ -108,6 +111,7 @@ class FullLayer:
     ("c2", [(2048, 64), (1, 64)]),
     ("c3", [(16, 64), (512, 64), (1, 64), (32, 64)]),
     ("c4", [(1, 0), (1, 16), (1, 64), (1, 128), (16, 0), (16, 128), (256, 64), (4096, 128)]),
+    ("v1", [(9, 0), (2, 0), (5, 0)]),
 ])
 def test_full_size_layer(torch, name, runs):
     L = FullLayer(torch, name)

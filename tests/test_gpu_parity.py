@@ -186,6 +186,47 @@ def test_layer_matches_oracle(torch, K, N, r, g, asym, T):
         assert ok, (path, st)
 
 
+# ------------------------------------ per-tensor verify pass (Quasar)
+# Quasar summary, "Targeted quantization": the verify forward runs on int4
+# weights with one symmetric per-tensor scale; no compensator; a verify batch
+# is the drafted tokens plus one.
+@pytest.mark.parametrize("N,K", [(64, 512), (208, 1024), (16, 128)])
+def test_per_tensor_quantizer_bytes_match_oracle(torch, N, K):
+    note(f"per-tensor quantize N={N} K={K}")
+    rng = np.random.default_rng(N + K)
+    W = (rng.standard_normal((N, K)) * 0.02).astype(np.float32)
+    W[N // 3] = 0.0                                  # a zero row keeps the common scale
+    W[N // 2] *= 3.0                                 # the row holding the tensor's max
+    d = q.make_desc(K, N, 0, K, False, True)
+    wq, sc, zs = q.alloc_packed(d)
+    assert zs is None
+    q.spear_ec_quantize_rtn(d, to_dev_f32(W), wq, sc, zs)
+    torch.cuda.synchronize()
+    o_wq, o_sc, _ = oracle.quantize_rtn_per_tensor(W)
+    assert np.array_equal(from_dev_u32(wq), o_wq)
+    assert np.array_equal(sc.view(torch.int16).cpu().numpy().view(np.uint16), o_sc)
+
+
+@pytest.mark.parametrize("K,N,T", [(1024, 400, 2), (1024, 400, 5), (1024, 400, 9), (4096, 256, 9)])
+def test_per_tensor_verify_pass_matches_oracle(torch, K, N, T):
+    note(f"verify pass K={K} N={N} T={T}")
+    spec = synth.small_spec(K, N, 0, K, False, seed_base=9000 + K + T)
+    W = synth.weights(spec)
+    x = synth.activations(spec, T)
+    d = q.make_desc(K, N, 0, K, False, True)
+    wq, sc, zs = q.alloc_packed(d)
+    q.spear_ec_quantize_rtn(d, to_dev_f32(W), wq, sc, zs)
+    o_wq, o_sc, _ = oracle.quantize_rtn_per_tensor(W)
+    yref = oracle.forward(x, o_wq, o_sc, None, None, None, None, None, 1.0, K)
+    ws = q.alloc_workspace(d, T)
+    for fn in (q.spear_ec_linear, q.spear_ec_linear_decode):
+        y = torch.empty((T, N), dtype=torch.bfloat16, device="cuda")
+        fn(d, to_dev_bf16(x), wq, sc, zs, None, None, None, None, 1.0, y, ws)
+        torch.cuda.synchronize()
+        ok, st = check_bf16_output(from_dev_u16(y), yref)
+        assert ok, (fn.__name__, st)
+
+
 @pytest.mark.parametrize("K,N,r,g,asym", [(1024, 400, 32, 128, True), (512, 256, 16, 512, False)])
 def test_random_packed_bytes_through_both_paths(torch, K, N, r, g, asym):
     """Externally quantized weights (uniform random codes, scales and zero-points)."""

@@ -226,6 +226,51 @@ def test_quantizer_asymmetric_full_range_is_idempotent():
             assert np.array_equal(wq[n], wq2[n]) and sc[n, 0] == sc2[n, 0]
 
 
+# --------------------------------------------- per-tensor scales (Quasar)
+# Quasar summary, "Targeted quantization": one symmetric scaling factor per
+# tensor for the verify pass.
+def test_per_tensor_hand_example(golden):
+    e = golden["quant_per_tensor"]
+    W = np.array(e["W"], np.float32)
+    wq, sc, zs = oracle.quantize_rtn_per_tensor(W)
+    assert zs is None
+    assert [hex(int(w)) for w in wq[:, 0]] == [w.lower() for w in e["words"]]
+    assert np.all(sc == hx(e["scale_bits"]))
+    assert oracle.codes(wq, 8).tolist() == e["codes"]
+    assert oracle.dequant(wq, sc, None, 8, 8).tolist() == e["dequant"]
+
+
+def test_per_tensor_single_row_is_per_channel():
+    rng = np.random.default_rng(11)
+    for K in (8, 256, 1024):
+        W = (rng.standard_normal((1, K)) * 0.02).astype(np.float32)
+        a = oracle.quantize_rtn_per_tensor(W)
+        b = oracle.quantize_rtn(W, K, False)
+        assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+
+
+def test_per_tensor_scale_is_numpy_half_of_the_global_max_and_codes_are_nearest():
+    rng = np.random.default_rng(12)
+    W = (rng.standard_normal((24, 512)) * 0.02).astype(np.float32)
+    W[5] *= 4.0                                     # one row holds the tensor's max
+    wq, sc, _ = oracle.quantize_rtn_per_tensor(W)
+    want = np.array(np.float16(np.abs(W.astype(np.float64)).max() / 7.0)).view(np.uint16)
+    assert np.all(sc == want)
+    s = float(np.array(want).view(np.float16))
+    C = oracle.codes(wq, 512)
+    assert C.min() >= 1 and C.max() <= 15            # -8 is never needed
+    Wt = oracle.dequant(wq, sc, None, 512, 512)
+    assert np.max(np.abs(W - Wt)) <= s / 2           # nearest code, no clipping
+    # the rows without the max keep that common scale (not their own)
+    own = oracle.quantize_rtn(W[:1], 512, False)[1]
+    assert int(own[0, 0]) != int(want)
+
+
+def test_per_tensor_zero_tensor_gets_unit_scale():
+    wq, sc, _ = oracle.quantize_rtn_per_tensor(np.zeros((3, 16), np.float32))
+    assert np.all(sc == 0x3C00) and np.all(oracle.codes(wq, 16) == 8)
+
+
 def test_quantizer_zero_group_gets_unit_scale():
     W = np.zeros((2, 16), np.float32)
     for asym in (False, True):
