@@ -94,6 +94,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--config", default="c3", choices=sorted(WORKLOADS))
     ap.add_argument("--rank", type=int, default=None, help="override the compensator rank")
+    ap.add_argument("--mlp-gate", type=int, default=0, metavar="H",
+                    help="use the bottleneck-MLP gate of width H (0: the elementwise gate)")
     ap.add_argument("--copies", type=int, default=0, help="weight copies to rotate (0 = auto)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -140,6 +142,7 @@ def main():
     W = synth.weights(spec)
     X = synth.activations(spec, Ttot)
     A, B, gv, bv = synth.compensator(spec, r)
+    mlp = synth.mlp_gate(spec, r, args.mlp_gate) if args.mlp_gate and r else None
     desc = q.make_desc(K, N, r, g, asym, spec.per_tensor)
     wq0, sc0, zs0 = q.alloc_packed(desc, dev)
     q.spear_ec_quantize_rtn(desc, to_dev_f32(W, dev), wq0, sc0, zs0)
@@ -152,7 +155,8 @@ def main():
         layers.append(dict(
             wq=wq0.clone(), sc=sc0.clone(), zs=zs0.clone() if zs0 is not None else None,
             A=to_dev_bf16(A, dev) if r else None, B=to_dev_bf16(B, dev) if r else None,
-            g=to_dev_f32(gv, dev) if r else None, b=to_dev_f32(bv, dev) if r else None))
+            g=to_dev_f32(gv, dev) if r else None, b=to_dev_f32(bv, dev) if r else None,
+            mlp={k: to_dev_f32(v, dev) for k, v in mlp.items()} if mlp else None))
     xs, ys, off = [], [], 0
     for _, T in plan:
         xs.append(to_dev_bf16(X[off:off + T], dev))
@@ -169,8 +173,14 @@ def main():
         for j, (path, T) in enumerate(plan):
             if evs is not None:
                 evs[j].record(stream)
-            q.spear_ec_linear(desc, xs[j], L["wq"], L["sc"], L["zs"], L["A"], L["B"], L["g"],
-                              L["b"], spec.alpha, ys[j], ws, stream)
+            if L["mlp"] is not None:
+                m = L["mlp"]
+                q.spear_ec_linear_mlp_gate(desc, xs[j], L["wq"], L["sc"], L["zs"], L["A"], L["B"],
+                                           m["w1"], m["b1"], m["w2"], m["b2"], spec.alpha, ys[j],
+                                           ws, stream)
+            else:
+                q.spear_ec_linear(desc, xs[j], L["wq"], L["sc"], L["zs"], L["A"], L["B"],
+                                  L["g"], L["b"], spec.alpha, ys[j], ws, stream)
         if evs is not None:
             evs[len(plan)].record(stream)
 
@@ -237,6 +247,7 @@ def main():
         "config": {"workload": f"{args.config}: " + WORKLOADS[args.config]["text"],
                    "d_in": K, "d_out": N, "rank": r, "group_size": g,
                    "zero_points": asym, "per_tensor": spec.per_tensor,
+                   "gate": f"bottleneck MLP, hidden {args.mlp_gate}" if mlp else "elementwise",
                    "tokens_per_step": [T for _, T in plan],
                    "weight_copies_rotated": copies, "parallelism": "single GPU"},
         "calls": [{k: (round(v, 4) if isinstance(v, float) else v) for k, v in c.items()}
@@ -251,7 +262,7 @@ def main():
     out["setup_s"] = round(setup_s, 1)
 
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(spec, r, plan, X, A, B, gv, bv, unit)
+        out["cpu_baseline"] = cpu_baseline(spec, r, plan, X, A, B, gv, bv, unit, mlp)
     print(json.dumps(out), flush=True)
 
 
@@ -326,7 +337,7 @@ def load_traffic(config):
     return t.get("bytes_per_call", {})
 
 
-def cpu_baseline(spec, r, plan, X, A, B, gv, bv, unit):
+def cpu_baseline(spec, r, plan, X, A, B, gv, bv, unit, mlp=None):
     """The fp64 oracle on a bounded sample of the same layer: every token of
     the first call of the step, a slice of output rows.  Scaled to the unit
     of `value` by the algorithmic bytes (or flops) of that slice."""
@@ -341,7 +352,8 @@ def cpu_baseline(spec, r, plan, X, A, B, gv, bv, unit):
     t0 = time.time()
     wq, sc, zs = oracle.quantize_rtn_per_tensor(Wsl) if spec.per_tensor else oracle.quantize_rtn(Wsl, g, asym)
     t1 = time.time()
-    oracle.forward(x, wq, sc, zs, A if r else None, B[:rows] if r else None, gv, bv, spec.alpha, g)
+    oracle.forward(x, wq, sc, zs, A if r else None, B[:rows] if r else None, gv, bv, spec.alpha, g,
+                   mlp=mlp)
     t2 = time.time()
     secs = t2 - t1
     by = layer_bytes(K, rows, r, g, asym, T)

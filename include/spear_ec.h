@@ -142,6 +142,25 @@ int spear_ec_linear_prefill(const spear_ec_desc* desc, int32_t tokens, const voi
                             hipStream_t stream);
 
 /*
+ * The same layer with the gate as the bottleneck MLP the SPEAR summary
+ * (section 2.1 A) names: gamma(u) = sigmoid(W2 relu(W1 u + b1) + b2), so
+ * V = gamma(U) (.) U with U = X A^T, and Y = X W~^T + alpha V B^T.  hidden
+ * (1 .. 128) is the bottleneck width h; w1 fp32 [h][rank], b1 fp32 [h],
+ * w2 fp32 [rank][h], b2 fp32 [rank] (device pointers, 16-byte aligned,
+ * caller-owned; required when rank > 0, ignored with rank 0).  Every other
+ * argument, the dispatch (T <= 32 decode kernel, else prefill), the workspace
+ * and the status codes are those of spear_ec_linear; an unsupported hidden is
+ * SPEAR_EC_ERR_UNSUPPORTED.  relu is the reading of the bottleneck's
+ * activation (the pages give no formula).
+ */
+int spear_ec_linear_mlp_gate(const spear_ec_desc* desc, int32_t tokens, const void* x,
+                             const uint32_t* wq, const void* scales, const uint32_t* zeros,
+                             const void* A, const void* B, int32_t hidden, const float* w1,
+                             const float* b1, const float* w2, const float* b2, float alpha,
+                             void* y, void* workspace, size_t workspace_bytes,
+                             hipStream_t stream);
+
+/*
  * Round-to-nearest int4 quantization of fp32 weights w [d_out][d_in] into the
  * packed format above (offline preparation; SPEAR summary, section 3.1: RTN
  * with per-channel scales is the hardest setting the compensators target).

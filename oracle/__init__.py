@@ -69,6 +69,8 @@ def _load():
         lib.orc_forward_sampled.restype = None
         lib.orc_forward_effective_weight.argtypes = fwd + [P]
         lib.orc_forward_effective_weight.restype = None
+        lib.orc_set_mlp_gate.argtypes = [i32, P, P, P, P]
+        lib.orc_set_mlp_gate.restype = None
         _lib = lib
     return _lib
 
@@ -181,33 +183,59 @@ def _fwd_args(x, wq, scales, zeros, A, B, g, b):
     return x, wq, sc, zs, A, B, g, b, T, K, N, r
 
 
-def forward(x, wq, scales, zeros, A, B, g, b, alpha, group_size, return_uv=False):
-    """y (double [T][N]) of the compensated layer; x, A, B are bf16 bit arrays."""
+class _MlpGate:
+    """Context: the oracle's gate is the bottleneck MLP (w1 [h][r], b1 [h],
+    w2 [r][h], b2 [r], fp32) inside, the elementwise sigmoid after."""
+
+    def __init__(self, mlp):
+        self.arrays = None
+        if mlp is not None:
+            w1, b1, w2, b2 = (_c(mlp[k], np.float32) for k in ("w1", "b1", "w2", "b2"))
+            self.arrays = (w1, b1, w2, b2)
+
+    def __enter__(self):
+        if self.arrays is not None:
+            w1, b1, w2, b2 = self.arrays
+            _load().orc_set_mlp_gate(int(w1.shape[0]), _p(w1), _p(b1), _p(w2), _p(b2))
+
+    def __exit__(self, *exc):
+        if self.arrays is not None:
+            _load().orc_set_mlp_gate(0, None, None, None, None)
+
+
+def forward(x, wq, scales, zeros, A, B, g, b, alpha, group_size, return_uv=False, mlp=None):
+    """y (double [T][N]) of the compensated layer; x, A, B are bf16 bit arrays.
+    mlp: None (elementwise gate from g, b) or dict(w1, b1, w2, b2) (bottleneck
+    MLP gate; g and b are then unused)."""
     x, wq, sc, zs, A, B, g, b, T, K, N, r = _fwd_args(x, wq, scales, zeros, A, B, g, b)
     y = np.empty((T, N), np.float64)
     u = np.empty((T, max(r, 1)), np.float64)
     v = np.empty((T, max(r, 1)), np.float64)
-    _load().orc_forward(T, K, N, r, group_size, _p(x), _p(wq), _p(sc), _p(zs), _p(A), _p(B),
-                        _p(g), _p(b), float(alpha), _p(y), _p(u), _p(v))
+    with _MlpGate(mlp):
+        _load().orc_forward(T, K, N, r, group_size, _p(x), _p(wq), _p(sc), _p(zs), _p(A), _p(B),
+                            _p(g), _p(b), float(alpha), _p(y), _p(u), _p(v))
     if return_uv:
         return y, u[:, :r], v[:, :r]
     return y
 
 
-def forward_sampled(x, wq, scales, zeros, A, B, g, b, alpha, group_size, t_idx, n_idx):
+def forward_sampled(x, wq, scales, zeros, A, B, g, b, alpha, group_size, t_idx, n_idx, mlp=None):
     x, wq, sc, zs, A, B, g, b, T, K, N, r = _fwd_args(x, wq, scales, zeros, A, B, g, b)
     ti = _c(t_idx, np.int32)
     ni = _c(n_idx, np.int32)
     y = np.empty(ti.size, np.float64)
-    _load().orc_forward_sampled(T, K, N, r, group_size, _p(x), _p(wq), _p(sc), _p(zs), _p(A),
-                                _p(B), _p(g), _p(b), float(alpha), int(ti.size), _p(ti), _p(ni),
-                                _p(y))
+    with _MlpGate(mlp):
+        _load().orc_forward_sampled(T, K, N, r, group_size, _p(x), _p(wq), _p(sc), _p(zs), _p(A),
+                                    _p(B), _p(g), _p(b), float(alpha), int(ti.size), _p(ti),
+                                    _p(ni), _p(y))
     return y
 
 
-def forward_effective_weight(x, wq, scales, zeros, A, B, g, b, alpha, group_size):
+def forward_effective_weight(x, wq, scales, zeros, A, B, g, b, alpha, group_size, mlp=None):
     x, wq, sc, zs, A, B, g, b, T, K, N, r = _fwd_args(x, wq, scales, zeros, A, B, g, b)
     y = np.empty((T, N), np.float64)
-    _load().orc_forward_effective_weight(T, K, N, r, group_size, _p(x), _p(wq), _p(sc), _p(zs),
-                                         _p(A), _p(B), _p(g), _p(b), float(alpha), _p(y))
+    with _MlpGate(mlp):
+        _load().orc_forward_effective_weight(T, K, N, r, group_size, _p(x), _p(wq), _p(sc),
+                                             _p(zs), _p(A), _p(B), _p(g), _p(b), float(alpha),
+                                             _p(y))
     return y

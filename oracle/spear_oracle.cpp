@@ -244,14 +244,56 @@ double orc_sigmoid(double z) {
 
 // Rank-r projection of one token and its gate:
 //   u[j] = sum_k A[j,k] x[k];  v[j] = sigmoid(g[j] u[j] + b[j]) * u[j].
+// ---------------------------------------------------------------- the gate
+// gamma of one token's projection u (length r) into gam.  Default: the
+// elementwise sigmoid(g_j u_j + b_j) (the fixed reading of the gate).  After
+// orc_set_mlp_gate(h, ...) with h > 0: the bottleneck MLP the SPEAR summary
+// (section 2.1 A) names as the gate,
+//     gamma_j = sigmoid(b2_j + sum_k W2[j,k] relu(b1_k + sum_i W1[k,i] u_i)),
+// W1 fp32 [h][r], b1 [h], W2 [r][h], b2 [r] (relu is the reading of its
+// activation).  The setting stays until the next call; h = 0 restores the
+// elementwise gate.
+static int g_mlp_h = 0;
+static const float *g_w1 = nullptr, *g_b1 = nullptr, *g_w2 = nullptr, *g_b2 = nullptr;
+
+void orc_set_mlp_gate(int h, const float* w1, const float* b1, const float* w2, const float* b2) {
+  g_mlp_h = h > 0 ? h : 0;
+  g_w1 = w1;
+  g_b1 = b1;
+  g_w2 = w2;
+  g_b2 = b2;
+}
+
+static void gate(const double* u, int r, const float* gv, const float* bv, double* gam) {
+  if (g_mlp_h == 0) {
+    for (int j = 0; j < r; ++j) gam[j] = orc_sigmoid((double)gv[j] * u[j] + (double)bv[j]);
+    return;
+  }
+  const int h = g_mlp_h;
+  std::vector<double> hid(h);
+  for (int k = 0; k < h; ++k) {
+    double a = (double)g_b1[k];
+    for (int i = 0; i < r; ++i) a += (double)g_w1[(size_t)k * r + i] * u[i];
+    hid[k] = a > 0.0 ? a : 0.0;
+  }
+  for (int j = 0; j < r; ++j) {
+    double a = (double)g_b2[j];
+    for (int k = 0; k < h; ++k) a += (double)g_w2[(size_t)j * h + k] * hid[k];
+    gam[j] = orc_sigmoid(a);
+  }
+}
+
+// u = A x_t (exact bf16 products summed in double) and v = gamma(u) (.) u.
 static void project_and_gate(const double* xt, const uint16_t* A, const float* gv,
                              const float* bv, int r, int K, double* u, double* v) {
   for (int j = 0; j < r; ++j) {
     double acc = 0.0;
     for (int k = 0; k < K; ++k) acc += orc_bf16_to_double(A[(size_t)j * K + k]) * xt[k];
     u[j] = acc;
-    v[j] = orc_sigmoid((double)gv[j] * acc + (double)bv[j]) * acc;
   }
+  std::vector<double> gam(r > 0 ? r : 1);
+  gate(u, r, gv, bv, gam.data());
+  for (int j = 0; j < r; ++j) v[j] = gam[j] * u[j];
 }
 
 // The compensated layer for T tokens:
@@ -326,11 +368,12 @@ void orc_forward_effective_weight(int T, int K, int N, int r, int g,
   orc_dequant(wq, scales, zeros, N, K, g, Wt.data());
   for (int t = 0; t < T; ++t) {
     for (int k = 0; k < K; ++k) xt[k] = orc_bf16_to_double(x[(size_t)t * K + k]);
+    std::vector<double> u(r > 0 ? r : 1);
     for (int j = 0; j < r; ++j) {
-      double u = 0.0;
-      for (int k = 0; k < K; ++k) u += orc_bf16_to_double(A[(size_t)j * K + k]) * xt[k];
-      gam[j] = orc_sigmoid((double)gv[j] * u + (double)bv[j]);
+      u[j] = 0.0;
+      for (int k = 0; k < K; ++k) u[j] += orc_bf16_to_double(A[(size_t)j * K + k]) * xt[k];
     }
+    gate(u.data(), r, gv, bv, gam.data());
     for (int n = 0; n < N; ++n)
       for (int k = 0; k < K; ++k) {
         double c = 0.0;

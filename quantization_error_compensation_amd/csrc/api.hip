@@ -194,10 +194,17 @@ static int hip_status(hipError_t e, const char* what) {
 
 enum Path { kAuto, kDecode, kPrefill };
 
+// The bottleneck-MLP gate's arguments (hidden == 0: the elementwise gate).
+struct MlpGate {
+  int hidden;
+  const float *w1, *b1, *w2, *b2;
+};
+
 static int linear(Path path, const spear_ec_desc* d, int32_t tokens, const void* x,
                   const uint32_t* wq, const void* scales, const uint32_t* zeros, const void* A,
                   const void* B, const float* g, const float* b, float alpha, void* y,
-                  void* workspace, size_t workspace_bytes, hipStream_t stream) {
+                  void* workspace, size_t workspace_bytes, hipStream_t stream,
+                  const MlpGate& mlp = MlpGate{0, nullptr, nullptr, nullptr, nullptr}) {
   g_last_error[0] = 0;
   int rc = check_desc(d, true);
   if (rc) return rc;
@@ -209,12 +216,17 @@ static int linear(Path path, const spear_ec_desc* d, int32_t tokens, const void*
   const bool has_z = (d->flags & SPEAR_EC_ZEROS) != 0;
   if (!x || !wq || !scales || !y) return fail(SPEAR_EC_ERR_INVALID_ARGUMENT, "x, wq, scales and y are required");
   if (has_z && !zeros) return fail(SPEAR_EC_ERR_INVALID_ARGUMENT, "zeros is required with SPEAR_EC_ZEROS");
-  if (d->rank > 0 && (!A || !B || !g || !b))
+  const bool gmlp = mlp.hidden > 0 && d->rank > 0;
+  if (!gmlp && d->rank > 0 && (!A || !B || !g || !b))
     return fail(SPEAR_EC_ERR_INVALID_ARGUMENT, "A, B, g and b are required when rank > 0");
+  if (gmlp && (!A || !B || !mlp.w1 || !mlp.b1 || !mlp.w2 || !mlp.b2))
+    return fail(SPEAR_EC_ERR_INVALID_ARGUMENT, "A, B, w1, b1, w2 and b2 are required when rank > 0");
   if (!workspace) return fail(SPEAR_EC_ERR_WORKSPACE, "workspace is NULL");
+  const bool eg = d->rank > 0 && !gmlp;
   const void* ptrs[] = {x, wq, scales, y, workspace, has_z ? zeros : nullptr,
-                        d->rank ? A : nullptr, d->rank ? B : nullptr, d->rank ? g : nullptr,
-                        d->rank ? b : nullptr};
+                        d->rank ? A : nullptr, d->rank ? B : nullptr, eg ? g : nullptr,
+                        eg ? b : nullptr, gmlp ? mlp.w1 : nullptr, gmlp ? mlp.b1 : nullptr,
+                        gmlp ? mlp.w2 : nullptr, gmlp ? mlp.b2 : nullptr};
   for (const void* p : ptrs)
     if (p && !aligned16(p)) return fail(SPEAR_EC_ERR_MISALIGNED, "a pointer is not 16-byte aligned");
   const bool decode = path == kDecode || (path == kAuto && tokens <= SPEAR_EC_DECODE_MAX_TOKENS);
@@ -229,8 +241,13 @@ static int linear(Path path, const spear_ec_desc* d, int32_t tokens, const void*
   a.zeros = has_z ? zeros : nullptr;
   a.A = d->rank ? A : nullptr;
   a.B = d->rank ? B : nullptr;
-  a.gv = d->rank ? g : nullptr;
-  a.bv = d->rank ? b : nullptr;
+  a.gv = eg ? g : nullptr;
+  a.bv = eg ? b : nullptr;
+  a.gh = gmlp ? mlp.hidden : 0;
+  a.w1 = gmlp ? mlp.w1 : nullptr;
+  a.b1 = gmlp ? mlp.b1 : nullptr;
+  a.w2 = gmlp ? mlp.w2 : nullptr;
+  a.b2 = gmlp ? mlp.b2 : nullptr;
   a.alpha = alpha;
   a.y = y;
   const WsPtrs wp = carve(workspace, wl);
@@ -285,6 +302,20 @@ int spear_ec_linear_prefill(const spear_ec_desc* desc, int32_t tokens, const voi
                             hipStream_t stream) {
   return linear(kPrefill, desc, tokens, x, wq, scales, zeros, A, B, g, b, alpha, y, workspace,
                 workspace_bytes, stream);
+}
+
+int spear_ec_linear_mlp_gate(const spear_ec_desc* desc, int32_t tokens, const void* x,
+                             const uint32_t* wq, const void* scales, const uint32_t* zeros,
+                             const void* A, const void* B, int32_t hidden, const float* w1,
+                             const float* b1, const float* w2, const float* b2, float alpha,
+                             void* y, void* workspace, size_t workspace_bytes,
+                             hipStream_t stream) {
+  if (desc && desc->rank > 0 && (hidden < 1 || hidden > 128)) {
+    g_last_error[0] = 0;
+    return fail(SPEAR_EC_ERR_UNSUPPORTED, "the gate's hidden width must be 1 .. 128");
+  }
+  return linear(kAuto, desc, tokens, x, wq, scales, zeros, A, B, nullptr, nullptr, alpha, y,
+                workspace, workspace_bytes, stream, MlpGate{hidden, w1, b1, w2, b2});
 }
 
 int spear_ec_quantize_rtn(const spear_ec_desc* desc, const float* w, uint32_t* wq, void* scales,

@@ -21,6 +21,7 @@ constexpr int kCounterSlots = 4096;   // int32 words at the head of the workspac
 constexpr int kCtrRankDone = 1;  // rank bands whose gated projection is published
 constexpr int kCtrExit = 2;      // decode workgroups that have finished
 constexpr int kCtrError = 3;     // set to 1 if a workgroup saw an inconsistent workspace
+constexpr int kCtrGateDone = 4;  // MLP gate: 1 once alpha * v of every rank is published
 constexpr int kCtrBand = 64;       // [64, 64 + bands): arrivals per band (rank bands first)
 constexpr int kCtrTile = 64;       // [64, 64 + tiles): prefill split-K arrivals per output tile
 constexpr int kMaxSlots = 1024;    // bound on resident decode workgroups used for sizing
@@ -93,6 +94,13 @@ struct LayerArgs {
   const void* B;
   const float* gv;
   const float* bv;
+  // bottleneck-MLP gate (gh > 0): gamma = sigmoid(W2 relu(W1 u + b1) + b2),
+  // W1 [gh][r], b1 [gh], W2 [r][gh], b2 [r]; gh == 0: elementwise gv, bv
+  int gh;
+  const float* w1;
+  const float* b1;
+  const float* w2;
+  const float* b2;
   float alpha;
   void* y;
 };

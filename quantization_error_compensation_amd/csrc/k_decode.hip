@@ -55,6 +55,11 @@ struct DecodeParams {
   const uint16_t* B;       // [N][r] bf16
   const float* gv;         // [r]
   const float* bv;         // [r]
+  int gh;                  // bottleneck-MLP gate width (0: elementwise gate gv, bv)
+  const float* w1;         // [gh][r]
+  const float* b1;         // [gh]
+  const float* w2;         // [r][gh]
+  const float* b2;         // [r]
   float alpha;
   float* part;             // [bands][maxseg][64][T4] partial sums
   float* wv32;             // [T][r] alpha * v
@@ -403,13 +408,14 @@ __device__ __forceinline__ void sum_parts(const DecodeParams& p, int band, int n
   }
 }
 
-// Finish a rank band: gate and publish alpha * v for this wave's 16 ranks.
+// Finish a rank band: gate and publish alpha * v for this wave's 16 ranks
+// (with the MLP gate, which needs every rank of a token, publish u itself).
 template <int MT>
 __device__ void finish_rank(const DecodeParams& p, int rb, const f32x4 (&u)[MT]) {
   const int lane = threadIdx.x & 63, wave = wave_id(), q = lane >> 4, c16 = lane & 15;
   const int j = 64 * rb + 16 * wave + c16;
   if (j >= p.r) return;
-  const float g = p.gv[j], b = p.bv[j];
+  const float g = p.gh > 0 ? 0.f : p.gv[j], b = p.gh > 0 ? 0.f : p.bv[j];
   const rsrc_t wr = make_rsrc(p.wv32, (uint32_t)p.T * p.r * 4);
   for (int mt = 0; mt < MT; ++mt)
     for (int i = 0; i < 4; ++i) {
@@ -417,9 +423,73 @@ __device__ void finish_rank(const DecodeParams& p, int rb, const f32x4 (&u)[MT])
       if (t < p.T) {
         const float uu = u[mt][i];
         bstore_dev(wr, (uint32_t)(t * p.r + j) * 4, 0,
-                   p.alpha * (sigmoidf_safe(fmaf(g, uu, b)) * uu));
+                   p.gh > 0 ? uu : p.alpha * (sigmoidf_safe(fmaf(g, uu, b)) * uu));
       }
     }
+}
+
+// n floats from src (plain or device-scope loads) into LDS, eight loads in
+// flight per thread so the copy costs about one memory round trip.
+template <bool DEV>
+__device__ __forceinline__ void copy_to_lds(const float* src, float* dst, int n) {
+  const rsrc_t r = make_rsrc(src, (uint32_t)n * 4);
+  for (int e0 = threadIdx.x; e0 < n; e0 += 8 * 256) {
+    float v[8];
+    for (int i = 0; i < 8; ++i) {
+      const uint32_t off = (uint32_t)(e0 + 256 * i) * 4;  // past n: zero, not stored
+      v[i] = DEV ? bload_dev(r, off, 0) : __builtin_bit_cast(float, bload4(r, off, 0));
+    }
+    for (int i = 0; i < 8; ++i)
+      if (e0 + 256 * i < n) dst[e0 + 256 * i] = v[i];
+  }
+}
+
+// The bottleneck-MLP gate (SPEAR summary, section 2.1 A), run once by the
+// workgroup that publishes the last rank band: every token's u (published
+// by the rank bands) goes to LDS, then
+//     h[t,k]       = relu(b1[k] + sum_i W1[k,i] u[t,i])
+//     alpha v[t,j] = alpha * sigmoid(b2[j] + sum_k W2[j,k] h[t,k]) * u[t,j]
+// in fp32 (sums in index order), written over u, and the gate counter is
+// raised.  W1 and W2 pass through LDS in chunks of whole rows.  lds: lds_floats
+// floats free for this workgroup, at least T (r + gh) + max(r, gh).
+__device__ void gate_mlp(const DecodeParams& p, uint8_t* lds, int lds_floats) {
+  const int tid = threadIdx.x, T = p.T, r = p.r, h = p.gh;
+  float* su = reinterpret_cast<float*>(lds);  // [T][r]
+  float* sh = su + T * r;                     // [T][h]
+  float* sw = sh + T * h;                     // weight rows
+  const int cap = lds_floats - T * (r + h);
+  const int c1 = min(h, cap / r), c2 = min(r, cap / h);  // rows per chunk of W1, W2
+  copy_to_lds<true>(p.wv32, su, T * r);
+  for (int k0 = 0; k0 < h; k0 += c1) {
+    const int nk = min(c1, h - k0);
+    copy_to_lds<false>(p.w1 + (size_t)k0 * r, sw, nk * r);
+    __syncthreads();
+    for (int e = tid; e < T * nk; e += 256) {
+      const int t = e / nk, k = e - t * nk;
+      float a = p.b1[k0 + k];
+      for (int i = 0; i < r; ++i) a = fmaf(sw[k * r + i], su[t * r + i], a);
+      sh[t * h + k0 + k] = fmaxf(a, 0.f);
+    }
+    __syncthreads();
+  }
+  const rsrc_t wr = make_rsrc(p.wv32, (uint32_t)T * r * 4);
+  for (int j0 = 0; j0 < r; j0 += c2) {
+    const int nj = min(c2, r - j0);
+    copy_to_lds<false>(p.w2 + (size_t)j0 * h, sw, nj * h);
+    __syncthreads();
+    for (int e = tid; e < T * nj; e += 256) {
+      const int t = e / nj, j = e - t * nj;
+      float a = p.b2[j0 + j];
+      for (int k = 0; k < h; ++k) a = fmaf(sw[j * h + k], sh[t * h + k], a);
+      bstore_dev(wr, (uint32_t)(t * r + j0 + j) * 4, 0,
+                 p.alpha * (sigmoidf_safe(a) * su[t * r + j0 + j]));
+    }
+    __syncthreads();
+  }
+  wait_vmem();
+  __syncthreads();
+  if (tid == 0) atomicAdd(&p.ctr[kCtrGateDone], 1);
+  __syncthreads();  // the LDS is the caller's again
 }
 
 // Row bands whose correction a correction workgroup adds (as an extra
@@ -430,12 +500,14 @@ __device__ __forceinline__ bool corrected(const DecodeParams& p, int nb) {
   return nb < p.cw * (kCorrBands / MT);
 }
 
-// Wait (bounded, error word on timeout) until every rank band has published
-// alpha * v.
+// Wait (bounded, error word on timeout) until alpha * v of every rank is
+// published: every rank band (elementwise gate) or the MLP gate's pass.
 __device__ __forceinline__ void wait_ranks(const DecodeParams& p) {
   if (threadIdx.x == 0) {
     int spins = 0;
-    while (load_dev(&p.ctr[kCtrRankDone]) < p.RB) {
+    const int* ctr = p.gh > 0 ? &p.ctr[kCtrGateDone] : &p.ctr[kCtrRankDone];
+    const int target = p.gh > 0 ? 1 : p.RB;
+    while (load_dev(ctr) < target) {
       __builtin_amdgcn_s_sleep(1);
       if (++spins > kSpinLimit) {
         atomicOr(&p.ctr[kCtrError], 1);
@@ -646,7 +718,9 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(DecodeParams p) {
         finish_rank<MT>(p, band, v);
         wait_vmem();
         __syncthreads();
-        if (tid == 0) atomicAdd(&p.ctr[kCtrRankDone], 1);
+        if (tid == 0) s_last = atomicAdd(&p.ctr[kCtrRankDone], 1) == p.RB - 1;
+        __syncthreads();
+        if (p.gh > 0 && s_last) gate_mlp(p, xlds, 2 * Burst<MT>::kBuf / 4);
       } else {
         if (p.r > 0 && !corr) {
           u32x4 bfr[kRankSteps];
@@ -666,6 +740,7 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(DecodeParams p) {
     wait_vmem();
     if (atomicAdd(&p.ctr[kCtrExit], 1) == p.P - 1) {
       store_dev(&p.ctr[kCtrRankDone], 0);
+      store_dev(&p.ctr[kCtrGateDone], 0);
       store_dev(&p.ctr[kCtrExit], 0);
     }
   }
@@ -706,6 +781,11 @@ hipError_t launch_decode(const Shape& s, const LayerArgs& a, const WsPtrs& w, hi
   p.B = static_cast<const uint16_t*>(a.B);
   p.gv = a.gv;
   p.bv = a.bv;
+  p.gh = a.gh;
+  p.w1 = a.w1;
+  p.b1 = a.b1;
+  p.w2 = a.w2;
+  p.b2 = a.b2;
   p.alpha = a.alpha;
   p.part = w.ypart;
   p.wv32 = w.wv32;

@@ -14,7 +14,11 @@
 // waves take contiguous runs of 128-column blocks; the split's partial u (and
 // row sum) goes to the workspace.  finish_kernel: one thread per (token, j)
 // sums the split partials in split order (deterministic), applies the gate
-// and writes alpha * v in fp32 and as a bf16 high/low pair.
+// and writes alpha * v in fp32 and as a bf16 high/low pair.  With the
+// bottleneck-MLP gate (SPEAR summary, section 2.1 A), which needs every rank
+// of a token, finish_mlp_kernel does the same with one workgroup per token:
+//     h[k] = relu(b1[k] + sum_i W1[k,i] u[i]),
+//     wv[j] = alpha * sigmoid(b2[j] + sum_k W2[j,k] h[k]) * u[j].
 #include "common.hpp"
 #include "internal.hpp"
 
@@ -26,6 +30,11 @@ struct ProjParams {
   const uint16_t* A;   // [r][K] bf16
   const float* gv;     // [r]
   const float* bv;     // [r]
+  int gh;              // bottleneck-MLP gate width (0: elementwise gate gv, bv)
+  const float* w1;     // [gh][r]
+  const float* b1;     // [gh]
+  const float* w2;     // [r][gh]
+  const float* b2;     // [r]
   float alpha;
   float* upart;        // [splits][T][r + 1]
   uint32_t* sblk;      // [KB][Tp][2]: block sums of x as bf16 (hi | mid << 16, lo)
@@ -150,6 +159,36 @@ hipError_t launch_rtx(const ProjParams& p, dim3 grid, hipStream_t st) {
   return hipGetLastError();
 }
 
+// One workgroup per token (r <= 128 < 129 threads' worth of ranks).
+__global__ __launch_bounds__(128) void finish_mlp_kernel(ProjParams p) {
+  __shared__ float su[128], sh[128];
+  const int t = blockIdx.x, tid = threadIdx.x;
+  const int R1 = p.r + 1;
+  for (int j = tid; j < R1; j += 128) {
+    float acc = 0.f;
+    for (int s = 0; s < p.splits; ++s) acc += p.upart[((size_t)s * p.T + t) * R1 + j];
+    if (j == p.r) p.stot[t] = acc;
+    else su[j] = acc;
+  }
+  __syncthreads();
+  for (int k = tid; k < p.gh; k += 128) {
+    float a = p.b1[k];
+    for (int i = 0; i < p.r; ++i) a = fmaf(p.w1[k * p.r + i], su[i], a);
+    sh[k] = fmaxf(a, 0.f);
+  }
+  __syncthreads();
+  for (int j = tid; j < p.r; j += 128) {
+    float a = p.b2[j];
+    for (int k = 0; k < p.gh; ++k) a = fmaf(p.w2[j * p.gh + k], sh[k], a);
+    const float wv = p.alpha * (sigmoidf_safe(a) * su[j]);
+    p.wv32[(size_t)t * p.r + j] = wv;
+    const uint32_t hi = f32_to_bf16_rne(wv);
+    const uint32_t lo = f32_to_bf16_rne(wv - __uint_as_float(hi << 16));
+    p.wvhi[(size_t)t * p.r + j] = (uint16_t)hi;
+    p.wvlo[(size_t)t * p.r + j] = (uint16_t)lo;
+  }
+}
+
 }  // namespace
 
 hipError_t launch_projection(const Shape& s, const LayerArgs& a, const WsPtrs& w,
@@ -160,6 +199,11 @@ hipError_t launch_projection(const Shape& s, const LayerArgs& a, const WsPtrs& w
   p.A = static_cast<const uint16_t*>(a.A);
   p.gv = a.gv;
   p.bv = a.bv;
+  p.gh = a.gh;
+  p.w1 = a.w1;
+  p.b1 = a.b1;
+  p.w2 = a.w2;
+  p.b2 = a.b2;
   p.alpha = a.alpha;
   p.upart = w.upart;
   p.sblk = w.sblk;
@@ -187,6 +231,10 @@ hipError_t launch_projection(const Shape& s, const LayerArgs& a, const WsPtrs& w
     default: return hipErrorInvalidValue;
   }
   if (e != hipSuccess) return e;
+  if (a.gh > 0 && s.r > 0) {
+    hipLaunchKernelGGL(finish_mlp_kernel, dim3(s.T), dim3(128), 0, st, p);
+    return hipGetLastError();
+  }
   const int elems = s.T * (s.r + 1);
   hipLaunchKernelGGL(finish_kernel, dim3((elems + 255) / 256), dim3(256), 0, st, p);
   return hipGetLastError();

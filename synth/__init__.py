@@ -33,6 +33,7 @@ from dataclasses import dataclass, field
 import numpy as np
 
 TENSOR_W, TENSOR_X, TENSOR_OUTLIERS, TENSOR_A, TENSOR_B, TENSOR_G, TENSOR_BIAS = 1, 2, 3, 4, 5, 6, 7
+TENSOR_W1, TENSOR_B1, TENSOR_W2, TENSOR_B2 = 8, 9, 10, 11   # bottleneck-MLP gate
 
 
 @dataclass(frozen=True)
@@ -120,6 +121,18 @@ def compensator(spec: LayerSpec, rank: int | None = None, salt: int = 0):
     b = np.zeros(R, np.float32)
     return (bf16_bits_from_f64(A[:r]), np.ascontiguousarray(bf16_bits_from_f64(B[:, :r])),
             g[:r].copy(), b[:r].copy())
+
+
+def mlp_gate(spec: LayerSpec, rank: int, hidden: int, salt: int = 0):
+    """Bottleneck-MLP gate parameters (fp32): w1 [h][r] ~ N(0, 1/r), b1 [h] ~
+    N(0, 0.1), w2 [r][h] ~ N(0, 1/h), b2 [r] ~ N(1, 0.5), so that the gate
+    varies between tokens around sigmoid(1)."""
+    w1 = _rng(spec, TENSOR_W1, salt).standard_normal((hidden, rank)) / np.sqrt(rank)
+    b1 = 0.1 * _rng(spec, TENSOR_B1, salt).standard_normal(hidden)
+    w2 = _rng(spec, TENSOR_W2, salt).standard_normal((rank, hidden)) / np.sqrt(hidden)
+    b2 = 1.0 + 0.5 * _rng(spec, TENSOR_B2, salt).standard_normal(rank)
+    return {k: np.ascontiguousarray(v, dtype=np.float32)
+            for k, v in (("w1", w1), ("b1", b1), ("w2", w2), ("b2", b2))}
 
 
 def small_spec(d_in: int, d_out: int, rank: int, group_size: int, asym: bool,

@@ -88,6 +88,28 @@ def test_validation_codes(lib, name):
                  ws_bytes=64) == binding.SPEAR_EC_ERR_WORKSPACE
 
 
+def _call_mlp(lib, desc, tokens, ptrs, hidden, ws_bytes=1 << 30):
+    get = lambda k: ptrs.get(k)
+    return lib.spear_ec_linear_mlp_gate(ctypes.byref(desc) if desc is not None else None, tokens,
+                                        get("x"), get("wq"), get("sc"), get("z"), get("A"),
+                                        get("B"), hidden, get("w1"), get("b1"), get("w2"),
+                                        get("b2"), 1.0, get("y"), get("ws"), ws_bytes, None)
+
+
+def test_mlp_gate_validation_codes(lib):
+    fake = {**FAKE, **{k: 0x10000 * (20 + i) for i, k in enumerate(["w1", "b1", "w2", "b2"])}}
+    good = q.make_desc(512, 512, 16, 512, False)
+    assert _call_mlp(lib, good, 0, fake, 8) == binding.SPEAR_EC_OK
+    for hidden in (0, 129, -1):
+        assert _call_mlp(lib, good, 4, fake, hidden) == binding.SPEAR_EC_ERR_UNSUPPORTED
+    for k in ("w1", "b1", "w2", "b2", "A"):
+        assert _call_mlp(lib, good, 4, {**fake, k: None}, 8) == binding.SPEAR_EC_ERR_INVALID_ARGUMENT
+    assert _call_mlp(lib, good, 4, {**fake, "w2": fake["w2"] + 4}, 8) == binding.SPEAR_EC_ERR_MISALIGNED
+    # rank 0: the gate is not used and may be absent
+    r0 = q.make_desc(512, 512, 0, 512, False)
+    assert _call_mlp(lib, r0, 0, {}, 0) == binding.SPEAR_EC_OK
+
+
 def test_decode_rejects_more_than_32_tokens(lib):
     d = q.make_desc(512, 512, 16, 512, False)
     assert _call(lib, "spear_ec_linear_decode", d, 33, FAKE, ws_bytes=1 << 40) == \

@@ -106,6 +106,33 @@ class FullLayer:
         return ok and finite and err_word == 0, dict(st, finite=finite, err_word=err_word)
 
 
+def test_full_size_mlp_gate_c3(torch):
+    """The 70B down-projection with the bottleneck-MLP gate (h = 16): decode
+    with the correction workgroups (T = 16, 1) and prefill (T = 512), sampled
+    against the oracle."""
+    L = FullLayer(torch, "c3")
+    spec = L.spec
+    m = synth.mlp_gate(spec, spec.rank, 16)
+    dm = {k: to_dev_f32(v) for k, v in m.items()}
+    for i, T in enumerate((16, 1, 512)):
+        x = synth.activations(spec, T)
+        A, B, _, _ = synth.compensator(spec)
+        desc = q.make_desc(L.K, L.N, spec.rank, L.g, L.asym)
+        y = torch.empty((T, L.N), dtype=torch.bfloat16, device="cuda")
+        ws = q.alloc_workspace(desc, T)
+        note(f"  MLP gate T={T}")
+        q.spear_ec_linear_mlp_gate(desc, to_dev_bf16(x), L.d_wq, L.d_sc, L.d_zs, to_dev_bf16(A),
+                                   to_dev_bf16(B), dm["w1"], dm["b1"], dm["w2"], dm["b2"],
+                                   spec.alpha, y, ws)
+        torch.cuda.synchronize()
+        assert int(ws[:16].view(torch.int32)[3].item()) == 0
+        ti, ni = sample_points(T, L.N, 200, 700 + i)
+        yref = oracle.forward_sampled(x, L.o_wq, L.o_sc, L.o_zs, A, B, None, None, spec.alpha,
+                                      L.g, ti, ni, mlp=m)
+        ok, st = check_sampled(from_dev_u16(y), ti, ni, yref)
+        assert ok, (T, st)
+
+
 @pytest.mark.parametrize("name,runs", [
     ("c1", [(1, 32), (8, 32), (32, 32)]),
     ("c2", [(2048, 64), (1, 64)]),

@@ -227,6 +227,43 @@ def test_per_tensor_verify_pass_matches_oracle(torch, K, N, T):
         assert ok, (fn.__name__, st)
 
 
+# ------------------------------------------------- bottleneck-MLP gate
+# SPEAR summary, section 2.1 A: the gate is a bottleneck MLP,
+# sigmoid(W2 relu(W1 u + b1) + b2) here.  Decode (rank bands, the MLP pass of
+# the last rank band, correction) and prefill (one finishing workgroup per
+# token) against the oracle; r = 128 has two rank bands.
+MLP_CASES = [
+    # K, N, r, h, g, asym, T
+    (1024, 400, 32, 8, 128, True, 1),
+    (1024, 400, 32, 8, 128, True, 16),
+    (1024, 400, 32, 8, 128, True, 33),
+    (1024, 400, 32, 1, 128, True, 7),
+    (768, 272, 64, 16, 768, False, 24),
+    (768, 272, 64, 16, 768, False, 130),
+    (2048, 96, 128, 32, 128, False, 5),
+    (2048, 96, 128, 128, 128, False, 40),
+]
+
+
+@pytest.mark.parametrize("K,N,r,h,g,asym,T", MLP_CASES)
+def test_mlp_gate_layer_matches_oracle(torch, K, N, r, h, g, asym, T):
+    note(f"MLP gate K={K} N={N} r={r} h={h} g={g} asym={asym} T={T}")
+    spec = synth.small_spec(K, N, r, g, asym, seed_base=11000 + K + T + h)
+    L = Layer(torch, spec, T)
+    m = synth.mlp_gate(spec, r, h)
+    dm = {k: to_dev_f32(v) for k, v in m.items()}
+    yref = oracle.forward(L.x, L.o_wq, L.o_sc, L.o_zs, L.A, L.B, None, None, L.alpha, L.g, mlp=m)
+    y = torch.empty((T, N), dtype=torch.bfloat16, device="cuda")
+    ws = q.alloc_workspace(L.desc, T)
+    for rep in range(2):   # the second call checks the gate counters were reset
+        q.spear_ec_linear_mlp_gate(L.desc, to_dev_bf16(L.x), L.d_wq, L.d_sc, L.d_zs, L.d_A, L.d_B,
+                                   dm["w1"], dm["b1"], dm["w2"], dm["b2"], L.alpha, y, ws)
+        torch.cuda.synchronize()
+        assert int(ws[:16].view(torch.int32)[3].item()) == 0
+        ok, st = check_bf16_output(from_dev_u16(y), yref)
+        assert ok, (rep, st)
+
+
 @pytest.mark.parametrize("K,N,r,g,asym", [(1024, 400, 32, 128, True), (512, 256, 16, 512, False)])
 def test_random_packed_bytes_through_both_paths(torch, K, N, r, g, asym):
     """Externally quantized weights (uniform random codes, scales and zero-points)."""

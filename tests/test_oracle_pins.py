@@ -343,6 +343,63 @@ def test_unit_gate_is_the_static_low_rank_correction(asym, g):
     assert np.allclose(y, _xf(L) @ Weff.T, rtol=1e-13, atol=1e-13)
 
 
+# ------------------------------------------------ bottleneck-MLP gate
+# SPEAR summary, section 2.1 A: the gate is a bottleneck MLP; the oracle's
+# form is sigmoid(W2 relu(W1 u + b1) + b2).  Pinned through cases that reduce
+# it to the (pinned) elementwise gate.
+def _mlp(r, h, seed):
+    return synth.mlp_gate(synth.small_spec(64, 40, r, 64, False, seed_base=seed), r, h)
+
+
+def test_mlp_gate_with_zero_w2_is_the_constant_elementwise_gate():
+    L = _layer(64, 40, 6, 3, 64, False, 21)
+    m = _mlp(6, 3, 21)
+    m["w2"][:] = 0.0
+    y = oracle.forward(L["x"], L["wq"], L["sc"], L["zs"], L["A"], L["B"], None, None, 0.8, 64,
+                       mlp=m)
+    ref = _fwd(L, alpha=0.8, g=np.zeros(6, np.float32), b=m["b2"])
+    assert np.allclose(y, ref, rtol=1e-15, atol=1e-15)
+
+
+def test_mlp_gate_with_identity_bottleneck_is_the_elementwise_gate():
+    # W1 = I, b1 = c large (relu is the identity there), W2 = diag(g),
+    # b2 = b - g c:  W2 relu(u + c) + b2 = g u + b.
+    L = _layer(64, 40, 6, 3, 64, True, 22)
+    c = 50.0
+    m = {"w1": np.eye(6, dtype=np.float32), "b1": np.full(6, c, np.float32),
+         "w2": np.diag(L["g"]).astype(np.float32),
+         "b2": (L["b"].astype(np.float64) - L["g"].astype(np.float64) * c).astype(np.float32)}
+    y = oracle.forward(L["x"], L["wq"], L["sc"], L["zs"], L["A"], L["B"], None, None, 0.9, 64,
+                       mlp=m)
+    # b2 = b - g c is rounded to fp32, so the two gates differ by that rounding
+    assert np.allclose(y, _fwd(L, alpha=0.9), rtol=1e-6, atol=1e-6)
+
+
+def test_mlp_gate_relu_clips_negative_bottleneck_inputs():
+    # b1 far below any W1 u: every hidden unit is clipped to 0 and the gate is
+    # sigmoid(b2) whatever W2 is (an identity activation would not give this).
+    L = _layer(64, 40, 6, 3, 64, False, 23)
+    m = _mlp(6, 4, 23)
+    m["b1"][:] = -1.0e6
+    y = oracle.forward(L["x"], L["wq"], L["sc"], L["zs"], L["A"], L["B"], None, None, 1.0, 64,
+                       mlp=m)
+    ref = _fwd(L, alpha=1.0, g=np.zeros(6, np.float32), b=m["b2"])
+    assert np.allclose(y, ref, rtol=1e-15, atol=1e-15)
+
+
+@pytest.mark.parametrize("h", [1, 3, 6])
+def test_mlp_gate_factored_path_equals_explicit_effective_weight(h):
+    L = _layer(48, 16, 6, 2, 16, True, 24 + h)
+    m = _mlp(6, h, 24 + h)
+    args = (L["x"], L["wq"], L["sc"], L["zs"], L["A"], L["B"], None, None, 0.7, 16)
+    y = oracle.forward(*args, mlp=m)
+    ye = oracle.forward_effective_weight(*args, mlp=m)
+    assert np.allclose(y, ye, rtol=1e-12, atol=1e-14)
+    # and the gate really depends on the token (not the constant sigmoid(b2))
+    yc = _fwd(L, alpha=0.7, g=np.zeros(6, np.float32), b=m["b2"])
+    assert not np.allclose(y, yc, rtol=1e-6, atol=1e-9)
+
+
 def test_correction_vanishes_when_projection_is_zero():
     L = _layer(64, 40, 6, 4, 64, False, 13)
     A = _bf(L["A"]).copy()
