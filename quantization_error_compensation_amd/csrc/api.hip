@@ -33,46 +33,27 @@ DecodePlan plan_decode(const Shape& s, int slots) {
   pl.bands = (s.N + kDecodeBandRows - 1) / kDecodeBandRows;
   pl.rank_bands = (s.r + 63) / 64;
   pl.units = (pl.bands + pl.rank_bands) * KB;
-  // A rank unit moves (ranks in the band) x 256 B of A against 4 KB of codes
-  // for a row unit; it is costed 1.25 times that so the rank bands, which
-  // every row finisher waits for, complete early.
+  // Costs in KB moved: a row unit is kDecodeBandRows x 64 B of codes, a rank
+  // unit (ranks in the band) x 256 B of A, costed 1.25 times that so the rank
+  // bands, which every row finisher waits for, complete early.
   const int ranks = std::min(std::max(s.r, 1), 64);
-  pl.rank_cost = std::max(1, (5 * ranks + 63) / 64);
-  pl.cost = (long long)pl.rank_bands * KB * pl.rank_cost + (long long)pl.bands * KB;
-  // At least 8 cost units (one burst of row blocks) per workgroup.  Since a
-  // rank unit costs at most 5, every workgroup's run then holds at least one
-  // unit, which the kernel's count of the workgroups sharing a band relies on.
+  pl.row_cost = kDecodeBandRows / 16;
+  pl.rank_cost = std::max(1, (5 * ranks + 15) / 16);
+  pl.cost = (long long)pl.rank_bands * KB * pl.rank_cost + (long long)pl.bands * KB * pl.row_cost;
+  // At least twice the dearest unit per workgroup: a run of cost C >= that
+  // unit's cost always holds a unit, which the kernel's count of the
+  // workgroups sharing a band relies on.
+  const int umax = std::max(pl.row_cost, pl.rank_cost);
   auto wgs = [&](int sl) {
-    long long P = std::min<long long>(sl, std::max<long long>(1, pl.cost / 8));
+    long long P = std::min<long long>(sl, std::max<long long>(1, pl.cost / (2 * umax)));
     return (int)std::max<long long>(1, std::min<long long>(P, pl.units));
   };
   pl.workgroups = wgs(std::min(std::max(slots, 1), kMaxSlots));
   // A band of cost Cb meets at most ceil(Cb * P / cost) + 1 workgroup runs;
-  // the bound grows with P, so the workspace is sized for the largest P.  A
-  // row band may take one more partial, the correction.
+  // the bound grows with P, so the workspace is sized for the largest P.
   const long long pmax = wgs(kMaxSlots);
-  const long long cb = (long long)KB * std::max(pl.rank_cost, 1);
-  pl.maxseg = (int)std::min<long long>(pmax, (cb * pmax + pl.cost - 1) / pl.cost + 1) +
-              (s.r > 0 ? 1 : 0);
-  // Correction workgroups: those whose runs end within the rank units (the
-  // kernel's unit_begin, evaluated on the host).  They finish their share
-  // early and add alpha v B^T to row bands while the rest still stream, so
-  // those bands' finishers do not wait for the rank bands.
-  // Only worth it when every workgroup streams a long run (its rank work and
-  // the correction then end well before the row bands): at least 32 cost
-  // units per workgroup.
-  pl.correction_wgs = 0;
-  if (s.r > 0 && pl.cost >= 32LL * pl.workgroups) {
-    const long long ru = (long long)pl.rank_bands * KB;
-    const long long rc = (long long)pl.rank_cost * pl.workgroups;
-    auto unit_begin = [&](long long w) {
-      const long long X = w * pl.cost;
-      if (X <= ru * rc) return (X + rc - 1) / rc;
-      return ru + (X - ru * rc + pl.workgroups - 1) / pl.workgroups;
-    };
-    while (pl.correction_wgs < pl.workgroups && unit_begin(pl.correction_wgs + 1) <= ru)
-      ++pl.correction_wgs;
-  }
+  const long long cb = (long long)KB * umax;
+  pl.maxseg = (int)std::min<long long>(pmax, (cb * pmax + pl.cost - 1) / pl.cost + 1);
   return pl;
 }
 
@@ -118,7 +99,8 @@ Workspace layout(const Shape& s, bool decode) {
     w.wvhi = w.wvlo = w.sblk = w.stot = w.upart = o;
     w.ypart = o;
     const size_t T4 = (T + 3) & ~(size_t)3;  // tokens rounded up to a multiple of 4
-    o = up256(o + sizeof(float) * (size_t)(dp.bands + dp.rank_bands) * dp.maxseg * T4 * 64);
+    o = up256(o + sizeof(float) * (size_t)(dp.bands + dp.rank_bands) * dp.maxseg * T4 *
+                       kDecodeBandRows);
   } else {
     const ProjPlan pp = plan_projection(s);
     const size_t Tp = (size_t)pp.tiles * kProjTokens;

@@ -9,7 +9,9 @@
 namespace spear {
 
 constexpr int kBlockK = 128;          // K block: one scale group (g = 128) or a slice of a row
-constexpr int kDecodeBandRows = 64;   // output rows per decode workgroup
+constexpr int kDecodeWaves = 8;                     // waves per decode workgroup, 16 rows each
+constexpr int kDecodeBandRows = 16 * kDecodeWaves;  // output rows per decode row band
+constexpr int kDecodeOccupancy = 1;                 // decode workgroups per compute unit
 constexpr int kProjTokens = 32;       // tokens per projection workgroup (prefill path)
 constexpr int kPrefillBM = 128;       // tokens per prefill tile
 constexpr int kPrefillBN = 256;       // output rows per prefill tile
@@ -41,16 +43,15 @@ struct ProjPlan {
 
 // Work split of the fused decode kernel (stream-K over band x block units).
 struct DecodePlan {
-  int bands;       // 64-row output bands
+  int bands;       // output bands of kDecodeBandRows rows
   int rank_bands;  // 64-rank bands of A
   int units;       // (bands + rank_bands) * K/128
-  int rank_cost;   // cost of one rank unit (a row unit costs 1)
+  int row_cost;    // cost of one row unit (its KB of codes)
+  int rank_cost;   // cost of one rank unit (1.25 x its KB of A)
   long long cost;  // total cost of all units
   int workgroups;  // persistent workgroups, each a run of units of equal cost
   int maxseg;      // bound on the partial sums of one band (any P up to kMaxSlots): the
-                   // workgroups sharing it, plus the correction partial when r > 0
-  int correction_wgs;  // the first workgroups, whose runs hold rank units only; they add
-                       // alpha v B^T to the row bands as partials (0: the finishers do)
+                   // workgroups sharing it
 };
 
 // Work split of the prefill GEMM: output tiles of kPrefillBM x kPrefillBN,

@@ -6,32 +6,35 @@
 // streams the packed weights once, computes the rank-r projection of every
 // token once, gates it, and adds alpha * B * v before the single bf16 store.
 //
-// Work.  A "band" is either 64 output rows of packed codes or 64 rows (ranks)
-// of A; a "unit" is one 128-column block of one band.  Rank bands come first
-// in the unit order.  A unit of a rank band moves 16 KB of bf16, a row unit
-// 4 KB of codes, so units carry a cost and the P persistent workgroups each
-// take a contiguous run of units of equal cost (stream-K).  A workgroup walks
+// Work.  A "band" is either BR = 16 x (waves per workgroup) output rows of
+// packed codes or 64 rows (ranks) of A; a "unit" is one 128-column block of
+// one band.  Rank bands come first in the unit order.  Units carry a cost
+// (the KB they move, 1.25 times that for rank units) and the P persistent
+// workgroups each take a contiguous run of units of equal cost (stream-K).  A workgroup walks
 // its run band segment by band segment.  A band covered by several
 // workgroups has its partial sums combined by whichever arrives last (in
 // segment order, so results are deterministic); partial sums move through
 // device-scope stores and loads (coherent across XCDs, no L2-wide fence).
 //
-// Inside a segment the four waves of a workgroup own one 16-row tile each
-// and walk the same K blocks in bursts of NS blocks:
+// Inside a row segment each wave of a workgroup owns one 16-row tile and all
+// walk the same K blocks in bursts of NS blocks (tall bands and short bursts:
+// x is read from L2 once per BR rows, and few loads queue per compute unit):
 //   * every load of a burst (x, codes or A rows, metadata) is issued one
 //     burst ahead, into registers, so it is in flight while the previous
 //     burst computes;
-//   * x of the burst is loaded once per workgroup (each wave 4 tokens x
-//     256 B per instruction, full cache lines), permuted into the
-//     matrix-core K order and written to a double-buffered LDS area; one
-//     barrier per burst publishes it to all four waves;
-//   * codes: 16 bytes per lane per block (16 rows x 64 B per instruction),
-//     all NS blocks issued back to back; bf16 operands 128 + c by byte
-//     permutes;
-//   * group scales and zero-points: staged per 32-block chunk in each wave's
-//     LDS area with loads that cover whole runs of a row's metadata;
-//   * matrix cores 16x16x32: tokens (padded to 16 or 32) x 16 rows x 32 K; a
-//     ones-operand product gives the block sums of x that remove the offset.
+//   * x of the burst is loaded once per workgroup (4 tokens x 256 B per
+//     instruction, full cache lines, spread over the waves), permuted into
+//     the matrix-core K order and written to a double-buffered LDS area with
+//     the block sums of x (vector adds and a 16-lane DPP tree); one barrier
+//     per burst publishes both to all waves;
+//   * codes: 16 bytes per lane per block (16 rows x 64 B per instruction);
+//     bf16 operands 128 + c by byte permutes;
+//   * group scale and zero-point word of the lane's row: one small load each
+//     per block, straight into registers;
+//   * matrix cores 16x16x32: tokens (padded to 16 or 32) x 16 rows x 32 K;
+//     the block sums remove the 128 + z offset in fp32.
+// In a rank segment the waves form W / 4 phases of four 16-rank tiles; phase
+// f takes block f of each burst and the phases are summed in LDS at the end.
 // The band finisher adds alpha * B * v as a small K = r matrix-core product
 // (v split into bf16 high and low parts) and stores y.
 //
@@ -61,33 +64,41 @@ struct DecodeParams {
   const float* w2;         // [r][gh]
   const float* b2;         // [r]
   float alpha;
-  float* part;             // [bands][maxseg][64][T4] partial sums
+  float* part;             // [bands][maxseg][BR][T4] partial sums
   float* wv32;             // [T][r] alpha * v
   int* ctr;                // counter words
   uint16_t* y;             // [T][N] bf16
   int T, K, N, r, G, ZW, has_z;
   int KB;                  // 128-column blocks per row
   int RB;                  // rank bands (64 ranks each)
-  int NB;                  // row bands (64 rows each)
+  int NB;                  // row bands (BR rows each)
   int P;                   // workgroups
-  int rank_cost;           // cost of a rank unit; a row unit costs 1
+  int row_cost;            // cost of a row unit
+  int rank_cost;           // cost of a rank unit
   long long ctot;          // total cost of all units
   int maxseg;              // bound on the partial sums of one band
-  int cw;                  // correction workgroups (the first cw, whose runs hold rank
-                           // units only): each adds alpha v B^T to up to
-                           // kCorrBands / MT row bands as one more partial
 };
+
+constexpr int W = kDecodeWaves;        // waves per workgroup
+constexpr int BR = kDecodeBandRows;    // rows of a row band (16 per wave)
+constexpr int PH = W / 4;              // phases of a rank segment (4 tiles of 16 ranks each)
+static_assert(W == 8 || W == 16, "a workgroup is 8 or 16 waves");
+constexpr int kThreads = 64 * W;
 
 constexpr int XROW = 272;            // LDS row of one token: 256 B + 16 B pad
 constexpr int kSpinLimit = 1 << 20;  // bounded wait (about a second)
 
-// Blocks per burst: 8 (row bands) / 4 (rank bands) up to 16 tokens, half that
-// up to 32 tokens, so one LDS buffer of x always holds 128 token-blocks.
+// Blocks per burst: 4 in row segments up to 16 tokens (2 above, for
+// registers), one per phase in rank segments.  One
+// x buffer holds [kMax][16 MT tokens][XROW] of x, then the block sums of x
+// [kMax][16 MT] fp32.
 template <int MT>
 struct Burst {
-  static constexpr int kRow = MT == 1 ? 8 : 4;
-  static constexpr int kRank = kRow / 2;
-  static constexpr int kBuf = kRow * 16 * MT * XROW;  // bytes of one x buffer
+  static constexpr int kRow = MT == 1 ? 4 : 2;
+  static constexpr int kRank = PH;
+  static constexpr int kMax = kRow > kRank ? kRow : kRank;
+  static constexpr int kSums = kMax * 16 * MT * XROW;  // byte offset of the block sums
+  static constexpr int kBuf = kSums + kMax * 16 * MT * 4;  // bytes of one x buffer
 };
 
 // ------------------------------------------------------------- partition
@@ -96,14 +107,15 @@ struct Burst {
 // unit u.
 __device__ __forceinline__ long long cost_prefix(const DecodeParams& p, long long u) {
   const long long ru = (long long)p.RB * p.KB;
-  return u <= ru ? u * p.rank_cost : ru * p.rank_cost + (u - ru);
+  return u <= ru ? u * p.rank_cost : ru * p.rank_cost + (u - ru) * p.row_cost;
 }
 __device__ __forceinline__ long long unit_begin(const DecodeParams& p, int w) {
   const long long X = (long long)w * p.ctot;
   const long long ru = (long long)p.RB * p.KB;
   const long long rc = (long long)p.rank_cost * p.P;
+  const long long wc = (long long)p.row_cost * p.P;
   if (X <= ru * rc) return (X + rc - 1) / rc;
-  return ru + (X - ru * rc + p.P - 1) / p.P;
+  return ru + (X - ru * rc + wc - 1) / wc;
 }
 __device__ __forceinline__ int owner_of(const DecodeParams& p, long long u) {
   return (int)(cost_prefix(p, u) * p.P / p.ctot);
@@ -111,38 +123,75 @@ __device__ __forceinline__ int owner_of(const DecodeParams& p, long long u) {
 
 // ------------------------------------------------------------- x staging
 // x of blocks [b, b + NS) into an LDS buffer [NS][16*MT tokens][XROW], each
-// 16-byte piece already in the matrix-core K order.  Wave w loads tokens
-// 4w + 16m .. +3 (lane: token 4w + 16m + l/16, piece l%16).  Every wave
-// issues the same loads whatever T is, so the count of loads in flight, and
-// with it every wait, is path-independent: lanes of tokens past T, and all
-// lanes when live is false, load from past the end of the buffer, which
-// reads zeros without a memory access.
+// 16-byte piece already in the matrix-core K order.  The burst is NS x 4MT
+// pieces of 4 tokens x 256 B; piece e = k W + w (block e / 4MT, tokens
+// 4 (e % 4MT) .. +3) is load k of wave w (lane: token + l/16, 16 B l%16).
+// Every wave issues the same loads whatever T is, so the count of loads in
+// flight, and with it every wait, is path-independent: lanes of tokens past
+// T, pieces past the burst, blocks past the segment and all lanes when live
+// is false load from past the end of the buffer, which reads zeros without a
+// memory access.  A block past the segment is then computed with x = 0 (it
+// adds nothing): skipping it would leave its registers unwaited on a path
+// the compiler cannot rule out, and it then waits for every load at the top
+// of the loop instead.
 template <int MT, int NS>
 struct XStage {
-  u32x4 g[NS][MT];
+  static constexpr int kPieces = NS * 4 * MT;
+  static constexpr int kLoads = (kPieces + W - 1) / W;
+  u32x4 g[kLoads];
 };
 
 template <int MT, int NS>
 __device__ __forceinline__ void x_issue(const DecodeParams& p, int wave, int lane, int b, int hi,
                                         bool live, XStage<MT, NS>& s) {
+  using S = XStage<MT, NS>;
   const uint32_t xrowB = (uint32_t)p.K * 2;
   const rsrc_t xr = make_rsrc(p.x, (uint32_t)p.T * xrowB);
-  for (int m = 0; m < MT; ++m) {
-    const int t = 4 * wave + 16 * m + (lane >> 4);
-    const uint32_t vo = live && t < p.T ? (uint32_t)t * xrowB + 16u * (lane & 15) : 0x80000000u;
-    for (int i = 0; i < NS; ++i) s.g[i][m] = bload16(xr, vo, (uint32_t)min(b + i, hi - 1) * 256);
+  for (int k = 0; k < S::kLoads; ++k) {
+    const int e = k * W + wave, i = min(e / (4 * MT), NS - 1);
+    const int t = 4 * (e % (4 * MT)) + (lane >> 4);
+    const bool ok = live && e < S::kPieces && t < p.T && b + i < hi;
+    const uint32_t vo = ok ? (uint32_t)t * xrowB + 16u * (lane & 15) : 0x80000000u;
+    // (uniform: readfirstlane keeps the offset scalar, or the compiler loops)
+    s.g[k] = bload16(xr, vo, __builtin_amdgcn_readfirstlane((uint32_t)min(b + i, hi - 1) * 256));
   }
 }
 
-template <int MT, int NS>
+// Sum of a float over the 16 lanes of a row (every lane gets the total).
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float row16_sum(float v) {
+  v += dpp_f32<0xB1>(v);   // quad_perm 1,0,3,2
+  v += dpp_f32<0x4E>(v);   // quad_perm 2,3,0,1
+  v += dpp_f32<0x141>(v);  // row_half_mirror
+  v += dpp_f32<0x140>(v);  // row_mirror
+  return v;
+}
+
+// Store the burst's x into buf; with SUMS, also the sum of each token's 128
+// values of each block (fp32: each lane adds its 8 values in order, then the
+// 16 lanes of the token's row are added as a tree).
+template <int MT, int NS, bool SUMS>
 __device__ __forceinline__ void x_store(uint8_t* buf, int wave, int lane,
                                         const XStage<MT, NS>& s) {
-  for (int i = 0; i < NS; ++i)
-    for (int m = 0; m < MT; ++m) {
-      const int t = 4 * wave + 16 * m + (lane >> 4);
+  using S = XStage<MT, NS>;
+  float* sums = reinterpret_cast<float*>(buf + Burst<MT>::kSums);
+  for (int k = 0; k < S::kLoads; ++k) {
+    const int e = k * W + wave, i = e / (4 * MT);
+    const int t = 4 * (e % (4 * MT)) + (lane >> 4);
+    if (S::kPieces % W == 0 || e < S::kPieces) {
       *reinterpret_cast<u32x4*>(buf + (i * 16 * MT + t) * XROW + 16 * (lane & 15)) =
-          x_permute8(s.g[i][m]);
+          x_permute8(s.g[k]);
+      if constexpr (SUMS) {
+        float a = 0.f;
+        for (int j = 0; j < 4; ++j) a += bf16_lo(s.g[k][j]) + bf16_hi(s.g[k][j]);
+        a = row16_sum(a);
+        if ((lane & 15) == 0) sums[i * 16 * MT + t] = a;
+      }
     }
+  }
 }
 
 // Fragment (mt, j) of block i for lane (token c16 + 16 mt, K group q): piece
@@ -165,23 +214,59 @@ __device__ __forceinline__ void lds_barrier() {
   asm volatile("" ::: "memory");
 }
 
-// What one burst of a rank segment takes from memory: x and the A rows.
+// The burst loop of a segment [lo, hi) in bursts of ns blocks, stage s0
+// already issued for the first burst: two register stages in turn, the next
+// burst's loads issued before this one computes.  The loop has one exit (at
+// the bottom) and every stage that enters it is consumed in it, so the
+// compiler's wait counts stay exact; with two exits its merged exit path
+// reached the top of the loop with a stage never consumed, and it then waited
+// for every load there, on every burst.  The scheduling barriers keep the
+// next stage's loads ahead of the work on this one.  The stage issued past
+// the last burst (out of range: no memory access, returns at once) is waited
+// for at the end, so nothing is left in flight for the code that follows.
+template <class Stage, class Issue, class Consume>
+__device__ __forceinline__ void pipeline2(int lo, int hi, int ns, Stage& s0, Stage& s1,
+                                          Issue&& issue, Consume&& consume) {
+  const int nb = (hi - lo + ns - 1) / ns;  // bursts
+  int b = lo;
+  for (int k = 0; k + 1 < nb; k += 2, b += 2 * ns) {
+    issue(s1, b + ns);
+    __builtin_amdgcn_sched_barrier(0);
+    consume(s0, b);
+    issue(s0, b + 2 * ns);
+    __builtin_amdgcn_sched_barrier(0);
+    consume(s1, b + ns);
+  }
+  if (nb & 1) {  // last burst in s0
+    issue(s1, b + ns);
+    __builtin_amdgcn_sched_barrier(0);
+    consume(s0, b);
+  }
+  __builtin_amdgcn_s_waitcnt(0);
+}
+
+// What one burst of a rank segment takes from memory: x and, per wave, the
+// A rows of its tile in its phase's block.
 template <int MT, int NS>
 struct RankStage {
   XStage<MT, NS> x;
-  u32x4 a[NS][4];
+  u32x4 a[4];
 };
 
-// Ranks 64 rb + 16 wave + c16, blocks [lo, hi): u = x A^T over the segment.
-// Loads run one burst ahead, in two register stages, as in row segments.
+// Ranks 64 rb + 16 (wave % 4) + c16, blocks [lo, hi): u = x A^T over the
+// segment, in the waves of phase 0 (wave < 4) on return.  Loads run one burst
+// ahead, in two register stages, as in row segments; phase f = wave / 4
+// takes block b + f of the burst starting at b.
 template <int MT>
 __device__ void rank_segment(const DecodeParams& p, int rb, int lo, int hi, uint8_t* xlds,
                              int& burst, f32x4 (&uo)[MT]) {
   constexpr int NS = Burst<MT>::kRank;
+  static_assert(NS == PH, "one block per phase and burst");
   const int lane = threadIdx.x & 63, wave = wave_id(), q = lane >> 4, c16 = lane & 15;
-  // A tile of ranks j0 .. j0 + 15; a wave past r reads the last tile again
+  const int tile = wave & 3, ph = wave >> 2;
+  // A tile of ranks j0 .. j0 + 15; a tile past r reads the last tile again
   // (its u columns are never published)
-  const int j0 = min(64 * rb + 16 * wave, p.r - 16);
+  const int j0 = min(64 * rb + 16 * tile, p.r - 16);
   const uint32_t arowB = (uint32_t)p.K * 2;
   const rsrc_t ar = make_rsrc(p.A + (size_t)j0 * p.K, 16u * arowB);
   const uint32_t ao = (uint32_t)c16 * arowB + 64u * q;  // pieces 4q .. 4q + 3 of row c16
@@ -190,164 +275,226 @@ __device__ void rank_segment(const DecodeParams& p, int rb, int lo, int hi, uint
   auto issue = [&](RankStage<MT, NS>& s, int b) {
     const bool live = b < hi;  // a burst past the segment loads nothing
     x_issue<MT, NS>(p, wave, lane, b, hi, live, s.x);
-    const uint32_t av = live ? ao : 0x80000000u;
-    for (int i = 0; i < NS; ++i)
-      for (int j = 0; j < 4; ++j)
-        s.a[i][j] = bload16(ar, av + 16 * j, (uint32_t)min(b + i, hi - 1) * 256);
+    const uint32_t av = b + ph < hi ? ao : 0x80000000u;
+    for (int j = 0; j < 4; ++j)
+      s.a[j] = bload16(ar, av + 16 * j,
+                       __builtin_amdgcn_readfirstlane((uint32_t)min(b + ph, hi - 1) * 256));
   };
   auto consume = [&](RankStage<MT, NS>& s, int b) {
     uint8_t* buf = xlds + (burst & 1) * Burst<MT>::kBuf;
     ++burst;
-    x_store<MT, NS>(buf, wave, lane, s.x);
+    x_store<MT, NS, false>(buf, wave, lane, s.x);
     lds_barrier();
-#pragma unroll
-    for (int i = 0; i < NS; ++i) {
-      if (b + i < hi) {
-        u32x4 xf[MT][4];
-        x_frags<MT>(buf, i, lane, xf);
-        for (int j = 0; j < 4; ++j) {
-          const u32x4 ap = x_permute8(s.a[i][j]);
-          for (int mt = 0; mt < MT; ++mt) uo[mt] = mfma16x16x32(xf[mt][j], ap, uo[mt]);
-        }
+    {  // a block past the segment has x = 0 and A = 0: it adds nothing
+      u32x4 xf[MT][4];
+      x_frags<MT>(buf, ph, lane, xf);
+      for (int j = 0; j < 4; ++j) {
+        const u32x4 ap = x_permute8(s.a[j]);
+        for (int mt = 0; mt < MT; ++mt) uo[mt] = mfma16x16x32(xf[mt][j], ap, uo[mt]);
       }
     }
   };
 
   RankStage<MT, NS> s0, s1;
+  __builtin_amdgcn_s_waitcnt(0);  // as in row segments
   issue(s0, lo);
-  for (int b = lo;; b += 2 * NS) {
-    issue(s1, b + NS);
-    consume(s0, b);
-    if (b + NS >= hi) break;
-    issue(s0, b + 2 * NS);
-    consume(s1, b + NS);
-    if (b + 2 * NS >= hi) break;
+  pipeline2(lo, hi, NS, s0, s1, issue, consume);
+
+  // Phase sums, in phase order, through the x buffer the next burst fills
+  // (every wave has passed the barrier after its last read).
+  if constexpr (PH > 1) {
+    static_assert((PH - 1) * 4 * MT * 64 * 16 <= Burst<MT>::kBuf, "phase sums fit an x buffer");
+    f32x4* red = reinterpret_cast<f32x4*>(xlds + (burst & 1) * Burst<MT>::kBuf);
+    if (ph > 0)
+      for (int mt = 0; mt < MT; ++mt) red[(((ph - 1) * 4 + tile) * MT + mt) * 64 + lane] = uo[mt];
+    __syncthreads();
+    if (ph == 0)
+      for (int f = 1; f < PH; ++f)
+        for (int mt = 0; mt < MT; ++mt) uo[mt] += red[(((f - 1) * 4 + tile) * MT + mt) * 64 + lane];
+    __syncthreads();
   }
 }
 
 // -------------------------------------------------------------- row segment
-// Group scales and zero-points of a wave's 16 rows are staged per chunk of
-// kMetaChunk blocks in the wave's own LDS area: ms[16][kMetaChunk] fp16 bits
-// and mz[16][8] zero-point words (word w0 + k holds blocks 8(w0 + k) ..).
-// Each staging load covers 2 rows x 32 consecutive scales (or 16 rows x 4
-// words), so a row's metadata costs a few cache-line requests per chunk
-// rather than one per burst.
-constexpr int kMetaChunk = 32;
-constexpr int kMetaWave = 16 * kMetaChunk * 2 + 16 * 8 * 4;  // bytes per wave
+// Group scales and zero-points of a wave's 16 rows are staged in the wave's
+// own LDS area by chunks of C blocks counted from the segment start
+// (chunk j: blocks lo + C j .., C = 16 NS), two chunks at a time: slot j % 2
+// holds one 32-bit word per (row, block), the scale's fp16 bits in the low
+// half and -(128 + z) as fp16 (exact) in the high half, rows C + 4 words
+// apart (a burst's NS words are one 8- or 16-byte read).  The first chunk is
+// loaded with the segment's first burst; then each burst of chunk j loads
+// one row of chunk j + 1 (a scale and its zero-point word per lane), packed
+// and written to LDS when the burst computes.  Bursts never straddle a
+// chunk, and all loads are issued on every burst.
+template <int MT>
+struct Meta {
+  static constexpr int kChunk = 16 * Burst<MT>::kRow;  // one row of the next chunk per burst
+  static constexpr int kStride = kChunk + 4;           // words per row
+  static constexpr int kSlot = 16 * kStride;           // words per slot
+  static constexpr int kWave = 2 * kSlot * 4;          // bytes per wave
+  static_assert(kChunk <= 64, "an entry per lane");
+};
+
+// The packed word of one (row, block): scale bits s, zero-point word zw of
+// the block's group of eight (none: z = 8).
+__device__ __forceinline__ uint32_t meta_pack(uint32_t s, uint32_t zw, int blk, bool has_z) {
+  const uint32_t z = has_z ? (zw >> (4 * (blk & 7))) & 15u : 8u;
+  return (s & 0xFFFFu) | ((0xD800u | (z << 3)) << 16);  // fp16 of -(128 + z)
+}
 
 // What one burst of a row segment takes from memory: x (permuted into LDS
-// when the burst starts), the codes, and at the start of a metadata chunk the
-// chunk's scales and zero-points.  Each burst's loads are issued one burst
-// ahead, so they are in flight while the previous burst computes.
+// with its block sums when the burst starts), the codes, and one row of the
+// next metadata chunk.  Each burst's loads are issued one burst ahead, so
+// they are in flight while the previous burst computes; every load is
+// issued on every burst (out of range, with no memory access, past the
+// segment), so the compiler's wait counts stay exact.
 template <int MT, int NS>
 struct RowStage {
   XStage<MT, NS> x;
   u32x4 w[NS];
-  uint32_t sv[8], zv[2];
+  uint32_t ms, mz;
 };
 
-// Rows 64 band + 16 wave + c16 (this wave's tile), blocks [lo, hi): partial
-// y with the scales applied.
+// Rows BR band + 16 wave + c16 (this wave's tile), blocks [lo, hi): partial
+// y with the scales applied.  Per block and token the result is
+// s (P - (128 + z) S), P the matrix-core product with the 128 + c operands
+// and S the block sum of x.
 template <int MT, bool GROUPED>
 __device__ void row_segment(const DecodeParams& p, int band, int lo, int hi, uint8_t* xlds,
                             uint8_t* mlds, int& burst, f32x4 (&yo)[MT]) {
   constexpr int NS = Burst<MT>::kRow;
+  constexpr uint32_t kOut = 0x80000000u;
   const int lane = threadIdx.x & 63, wave = wave_id(), q = lane >> 4, c16 = lane & 15;
   // Tile of rows rc .. rc + 15; a tile past N (last band of an N that is not
-  // a multiple of 64) reads the last tile again and stores nothing.
-  const int rc = min(band * 64 + 16 * wave, p.N - 16);
+  // a multiple of BR) reads the last tile again and stores nothing.
+  const int rc = min(band * BR + 16 * wave, p.N - 16);
   const uint32_t wrowB = (uint32_t)p.K / 2;
   const rsrc_t wr = make_rsrc(p.wq + (size_t)rc * (p.K / 8), 16u * wrowB);
   const uint32_t wo = (uint32_t)c16 * wrowB + 16u * q;
-  const uint16_t* St = p.scales + (size_t)rc * p.G;
-  const uint32_t* Zt = p.zeros + (size_t)rc * p.ZW;
-  const u32x4 ones = {kBf16One, kBf16One, kBf16One, kBf16One};
-  uint16_t* ms = reinterpret_cast<uint16_t*>(mlds + wave * kMetaWave);
-  uint32_t* mz = reinterpret_cast<uint32_t*>(mlds + wave * kMetaWave + 16 * kMetaChunk * 2);
-  int c0 = lo, w0 = lo >> 3;  // first block and first zero-point word of the staged chunk
+  const rsrc_t sr = make_rsrc(p.scales + (size_t)rc * p.G, 16u * p.G * 2);
+  const rsrc_t zr = make_rsrc(p.zeros + (size_t)rc * p.ZW, p.has_z ? 16u * p.ZW * 4 : 0u);
+  using M = Meta<MT>;
+  uint32_t* mw = reinterpret_cast<uint32_t*>(mlds + wave * M::kWave);
+  // packed word of row n, block lo + C j + c: slot j & 1, [n][c]
+  auto mp_at = [&](int slot, int n, int c) { return mw + slot * M::kSlot + n * M::kStride + c; };
+  // this lane's entry of a chunk (lanes past C repeat an entry) and its block
+  // (clamped into the segment) in a chunk starting at cb
+  const int ment = lane % M::kChunk;
+  auto meta_blk = [&](int cb) { return min(cb + ment, hi - 1); };
+  // loads of row n (per lane) at block blk: scale bits, zero-point word
+  auto meta_scale = [&](int n, int blk) { return bload2(sr, (uint32_t)(n * p.G + blk) * 2, 0); };
+  auto meta_zero = [&](int n, int blk) { return bload4(zr, (uint32_t)(n * p.ZW + (blk >> 3)) * 4, 0); };
 
-  f32x4 acc[MT], ssum[MT];
-  for (int mt = 0; mt < MT; ++mt) acc[mt] = ssum[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  // acc: the grouped result; per-channel: one product accumulator per block
+  // of a burst (accb), summed at the end
+  f32x4 acc[MT], ssum[MT], accb[NS][MT];
+  for (int mt = 0; mt < MT; ++mt) {
+    acc[mt] = ssum[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int i = 0; i < NS; ++i) accb[i][mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
 
   auto issue = [&](RowStage<MT, NS>& s, int b) {
-    if (GROUPED && (b - lo) % kMetaChunk == 0) {
-      const int c1 = min(b + kMetaChunk, hi);
-      const int blk = min(b + (lane & 31), c1 - 1);
-      for (int k = 0; k < 8; ++k)
-        s.sv[k] = gload2(St, (uint32_t)((2 * k + (lane >> 5)) * p.G + blk) * 2);
-      for (int e = 0; e < 2; ++e) {
-        const int wd = min((b >> 3) + (lane & 3) + 4 * e, (c1 - 1) >> 3);
-        s.zv[e] = p.has_z ? gload4(Zt, (uint32_t)((lane >> 2) * p.ZW + wd) * 4) : 0x88888888u;
-      }
-    }
     const bool live = b < hi;  // a burst past the segment loads nothing
     x_issue<MT, NS>(p, wave, lane, b, hi, live, s.x);
-    const uint32_t wv = live ? wo : 0x80000000u;
-    for (int i = 0; i < NS; ++i) s.w[i] = bload16(wr, wv, (uint32_t)min(b + i, hi - 1) * 64);
+    const uint32_t wv = live ? wo : kOut;
+    for (int i = 0; i < NS; ++i)
+      s.w[i] = bload16(wr, wv, __builtin_amdgcn_readfirstlane((uint32_t)min(b + i, hi - 1) * 64));
+    if constexpr (GROUPED) {
+      const int k = (b - lo) / NS;  // burst index: row k % 16 of chunk k / 16 + 1
+      const int blk = meta_blk(lo + M::kChunk * (k / 16 + 1));
+      s.ms = meta_scale(k & 15, blk);
+      s.mz = meta_zero(k & 15, blk);
+    }
   };
 
   auto consume = [&](RowStage<MT, NS>& s, int b) {
     uint8_t* buf = xlds + (burst & 1) * Burst<MT>::kBuf;
+    const float* sums = reinterpret_cast<const float*>(buf + Burst<MT>::kSums);
     ++burst;
-    if (GROUPED && (b - lo) % kMetaChunk == 0) {
-      c0 = b;
-      w0 = b >> 3;
-      for (int k = 0; k < 8; ++k)
-        ms[(2 * k + (lane >> 5)) * kMetaChunk + (lane & 31)] = (uint16_t)s.sv[k];
-      for (int e = 0; e < 2; ++e) mz[(lane >> 2) * 8 + (lane & 3) + 4 * e] = s.zv[e];
-    }
-    x_store<MT, NS>(buf, wave, lane, s.x);
+    x_store<MT, NS, true>(buf, wave, lane, s.x);
     lds_barrier();
-#pragma unroll
-    for (int i = 0; i < NS; ++i) {
-      if (b + i >= hi) continue;
-      u32x4 xf[MT][4];
-      x_frags<MT>(buf, i, lane, xf);
-      u32x4 wb[4];
-      wb[0] = codes_to_bf16_offset(s.w[i].x);
-      wb[1] = codes_to_bf16_offset(s.w[i].y);
-      wb[2] = codes_to_bf16_offset(s.w[i].z);
-      wb[3] = codes_to_bf16_offset(s.w[i].w);
-      if constexpr (GROUPED) {
-        const int blk = b + i;
-        const float sc = half_bits_to_f32(ms[c16 * kMetaChunk + (blk - c0)]);
-        const uint32_t z = (mz[c16 * 8 + ((blk >> 3) - w0)] >> (4 * (blk & 7))) & 15u;
-        const float nz = -(float)(128u + z);
-        for (int mt = 0; mt < MT; ++mt) {
-          f32x4 sb = mfma16x16x32(xf[mt][0], ones, f32x4{0.f, 0.f, 0.f, 0.f});
-          f32x4 P = mfma16x16x32(xf[mt][0], wb[0], f32x4{0.f, 0.f, 0.f, 0.f});
-          for (int j = 1; j < 4; ++j) {
-            sb = mfma16x16x32(xf[mt][j], ones, sb);
-            P = mfma16x16x32(xf[mt][j], wb[j], P);
-          }
-          for (int v = 0; v < 4; ++v) acc[mt][v] = fmaf(sc, fmaf(nz, sb[v], P[v]), acc[mt][v]);
-        }
+    const int k = (b - lo) / NS, j = k / 16;  // this burst's chunk
+    uint32_t meta[NS];  // packed words of blocks b .. b + NS - 1 for row c16
+    if constexpr (GROUPED) {
+      if constexpr (NS == 4) {
+        const u32x4 m = *reinterpret_cast<const u32x4*>(mp_at(j & 1, c16, NS * (k & 15)));
+        for (int i = 0; i < NS; ++i) meta[i] = m[i];
       } else {
-        for (int mt = 0; mt < MT; ++mt)
-          for (int j = 0; j < 4; ++j) {
-            ssum[mt] = mfma16x16x32(xf[mt][j], ones, ssum[mt]);
-            acc[mt] = mfma16x16x32(xf[mt][j], wb[j], acc[mt]);
-          }
+        const u32x2 m = *reinterpret_cast<const u32x2*>(mp_at(j & 1, c16, NS * (k & 15)));
+        for (int i = 0; i < NS; ++i) meta[i] = m[i];
       }
     }
+    // Both blocks' operands first, then their matrix-core chains interleaved
+    // (two independent chains hide each other's latency), then the per-block
+    // scale fold.  A block past the segment has x = 0: it adds nothing.
+    u32x4 xf[NS][MT][4], wb[NS][4];
+    f32x4 sb[NS][MT];  // block sums of this lane's four tokens
+#pragma unroll
+    for (int i = 0; i < NS; ++i) {
+      x_frags<MT>(buf, i, lane, xf[i]);
+      for (int mt = 0; mt < MT; ++mt)
+        sb[i][mt] = *reinterpret_cast<const f32x4*>(sums + i * 16 * MT + 16 * mt + 4 * q);
+      wb[i][0] = codes_to_bf16_offset(s.w[i].x);
+      wb[i][1] = codes_to_bf16_offset(s.w[i].y);
+      wb[i][2] = codes_to_bf16_offset(s.w[i].z);
+      wb[i][3] = codes_to_bf16_offset(s.w[i].w);
+    }
+    if constexpr (GROUPED) {
+      f32x4 P[NS][MT];
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj)
+        for (int i = 0; i < NS; ++i)
+          for (int mt = 0; mt < MT; ++mt)
+            P[i][mt] = mfma16x16x32(xf[i][mt][jj], wb[i][jj],
+                                    jj == 0 ? f32x4{0.f, 0.f, 0.f, 0.f} : P[i][mt]);
+#pragma unroll
+      for (int i = 0; i < NS; ++i) {
+        const float sc = half_bits_to_f32((uint16_t)meta[i]);
+        const float nz = half_bits_to_f32((uint16_t)(meta[i] >> 16));  // -(128 + z)
+        for (int mt = 0; mt < MT; ++mt)
+          for (int v = 0; v < 4; ++v)
+            acc[mt][v] = fmaf(sc, fmaf(nz, sb[i][mt][v], P[i][mt][v]), acc[mt][v]);
+      }
+    } else {
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj)
+        for (int i = 0; i < NS; ++i)
+          for (int mt = 0; mt < MT; ++mt) accb[i][mt] = mfma16x16x32(xf[i][mt][jj], wb[i][jj], accb[i][mt]);
+      for (int i = 0; i < NS; ++i)
+        for (int mt = 0; mt < MT; ++mt) ssum[mt] += sb[i][mt];
+    }
+    // Row k % 16 of the next chunk (read from burst 16 (j + 1) on).
+    if constexpr (GROUPED)
+      *mp_at((j + 1) & 1, k & 15, ment) =
+          meta_pack(s.ms, s.mz, meta_blk(lo + M::kChunk * (j + 1)), p.has_z);
   };
 
   // Two stages in turn: while one burst computes, the next one loads.  The
   // stage past the segment's last burst is issued too, with its loads out of
   // range (no memory access): the number of loads in flight is then the same
-  // on every path, so the waits on each stage stay exact.
+  // on every path, so the waits on each stage stay exact.  The first chunk's
+  // metadata is requested with the first stage and stored in LDS before the
+  // loop.
   RowStage<MT, NS> s0, s1;
-  issue(s0, lo);
-  for (int b = lo;; b += 2 * NS) {
-    issue(s1, b + NS);
-    consume(s0, b);
-    if (b + NS >= hi) break;
-    issue(s0, b + 2 * NS);
-    consume(s1, b + NS);
-    if (b + 2 * NS >= hi) break;
+  // Nothing from before may be in flight when the loop starts: the compiler
+  // would otherwise guard the loop's first register writes with a wait for
+  // every load, on every burst.
+  __builtin_amdgcn_s_waitcnt(0);
+  if constexpr (GROUPED) {
+    uint32_t m0s[16], m0z[16];  // row n, this lane's entry
+    const int blk = meta_blk(lo);
+    for (int n = 0; n < 16; ++n) m0s[n] = meta_scale(n, blk);
+    for (int n = 0; n < 16; ++n) m0z[n] = meta_zero(n, blk);
+    issue(s0, lo);
+    for (int n = 0; n < 16; ++n) *mp_at(0, n, ment) = meta_pack(m0s[n], m0z[n], blk, p.has_z);
+  } else {
+    issue(s0, lo);
   }
+  pipeline2(lo, hi, NS, s0, s1, issue, consume);
 
   if constexpr (!GROUPED) {  // per-channel: one scale and one offset correction per row
+    for (int mt = 0; mt < MT; ++mt)
+      for (int i = 0; i < NS; ++i) acc[mt] += accb[i][mt];
     const int n = rc + c16;
     const float sc = half_bits_to_f32(p.scales[n]);
     const int z = p.has_z ? (int)(p.zeros[(size_t)n * p.ZW] & 15u) : 8;
@@ -359,18 +506,18 @@ __device__ void row_segment(const DecodeParams& p, int band, int lo, int hi, uin
 }
 
 // ------------------------------------------------------------ partial sums
-// [maxseg][64 columns][T4] floats per band (T4: T rounded up to a multiple
+// [maxseg][BR columns][T4] floats per band (T4: T rounded up to a multiple
 // of 4), written and read at device scope; a lane's four tokens of one
 // column form one 16-byte word, and words holding no token below T are
-// neither stored nor loaded.  Column c of a partial is row 64 band + c of a
-// row band, or rank 64 rb + c.
+// neither stored nor loaded.  Column c of a partial is row BR band + c of a
+// row band, or rank 64 rb + c (c < 64) of a rank band.
 __device__ __forceinline__ int tokens4(const DecodeParams& p) { return (p.T + 3) & ~3; }
 __device__ __forceinline__ rsrc_t part_rsrc(const DecodeParams& p, int band) {
-  const uint32_t seg = 64u * tokens4(p);  // floats of one partial
+  const uint32_t seg = (uint32_t)BR * tokens4(p);  // floats of one partial
   return make_rsrc(p.part + (size_t)band * p.maxseg * seg, (uint32_t)p.maxseg * seg * 4);
 }
 __device__ __forceinline__ uint32_t part_off(const DecodeParams& p, int sidx, int col, int t) {
-  return (uint32_t)(((sidx * 64 + col) * tokens4(p) + t) * 4);
+  return (uint32_t)(((sidx * BR + col) * tokens4(p) + t) * 4);
 }
 
 template <int MT>
@@ -384,12 +531,12 @@ __device__ __forceinline__ void put_part(const DecodeParams& p, int band, int si
   }
 }
 
-// The band's nseg partials summed in segment order; 16 / MT partials are in
+// The band's nseg partials summed in segment order; 8 / MT partials are in
 // flight at a time.
 template <int MT>
 __device__ __forceinline__ void sum_parts(const DecodeParams& p, int band, int nseg, int col,
                                           f32x4 (&v)[MT]) {
-  constexpr int CH = 16 / MT;
+  constexpr int CH = 8 / MT;
   const int q = (threadIdx.x & 63) >> 4;
   const rsrc_t r = part_rsrc(p, band);
   for (int mt = 0; mt < MT; ++mt) v[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -414,7 +561,7 @@ template <int MT>
 __device__ void finish_rank(const DecodeParams& p, int rb, const f32x4 (&u)[MT]) {
   const int lane = threadIdx.x & 63, wave = wave_id(), q = lane >> 4, c16 = lane & 15;
   const int j = 64 * rb + 16 * wave + c16;
-  if (j >= p.r) return;
+  if (wave >= 4 || j >= p.r) return;  // u is in the waves of phase 0
   const float g = p.gh > 0 ? 0.f : p.gv[j], b = p.gh > 0 ? 0.f : p.bv[j];
   const rsrc_t wr = make_rsrc(p.wv32, (uint32_t)p.T * p.r * 4);
   for (int mt = 0; mt < MT; ++mt)
@@ -433,14 +580,14 @@ __device__ void finish_rank(const DecodeParams& p, int rb, const f32x4 (&u)[MT])
 template <bool DEV>
 __device__ __forceinline__ void copy_to_lds(const float* src, float* dst, int n) {
   const rsrc_t r = make_rsrc(src, (uint32_t)n * 4);
-  for (int e0 = threadIdx.x; e0 < n; e0 += 8 * 256) {
+  for (int e0 = threadIdx.x; e0 < n; e0 += 8 * kThreads) {
     float v[8];
     for (int i = 0; i < 8; ++i) {
-      const uint32_t off = (uint32_t)(e0 + 256 * i) * 4;  // past n: zero, not stored
+      const uint32_t off = (uint32_t)(e0 + kThreads * i) * 4;  // past n: zero, not stored
       v[i] = DEV ? bload_dev(r, off, 0) : __builtin_bit_cast(float, bload4(r, off, 0));
     }
     for (int i = 0; i < 8; ++i)
-      if (e0 + 256 * i < n) dst[e0 + 256 * i] = v[i];
+      if (e0 + kThreads * i < n) dst[e0 + kThreads * i] = v[i];
   }
 }
 
@@ -464,7 +611,7 @@ __device__ void gate_mlp(const DecodeParams& p, uint8_t* lds, int lds_floats) {
     const int nk = min(c1, h - k0);
     copy_to_lds<false>(p.w1 + (size_t)k0 * r, sw, nk * r);
     __syncthreads();
-    for (int e = tid; e < T * nk; e += 256) {
+    for (int e = tid; e < T * nk; e += kThreads) {
       const int t = e / nk, k = e - t * nk;
       float a = p.b1[k0 + k];
       for (int i = 0; i < r; ++i) a = fmaf(sw[k * r + i], su[t * r + i], a);
@@ -477,7 +624,7 @@ __device__ void gate_mlp(const DecodeParams& p, uint8_t* lds, int lds_floats) {
     const int nj = min(c2, r - j0);
     copy_to_lds<false>(p.w2 + (size_t)j0 * h, sw, nj * h);
     __syncthreads();
-    for (int e = tid; e < T * nj; e += 256) {
+    for (int e = tid; e < T * nj; e += kThreads) {
       const int t = e / nj, j = e - t * nj;
       float a = p.b2[j0 + j];
       for (int k = 0; k < h; ++k) a = fmaf(sw[j * h + k], sh[t * h + k], a);
@@ -490,14 +637,6 @@ __device__ void gate_mlp(const DecodeParams& p, uint8_t* lds, int lds_floats) {
   __syncthreads();
   if (tid == 0) atomicAdd(&p.ctr[kCtrGateDone], 1);
   __syncthreads();  // the LDS is the caller's again
-}
-
-// Row bands whose correction a correction workgroup adds (as an extra
-// partial); kCorrBands / MT bands per correction workgroup.
-constexpr int kCorrBands = 8;
-template <int MT>
-__device__ __forceinline__ bool corrected(const DecodeParams& p, int nb) {
-  return nb < p.cw * (kCorrBands / MT);
 }
 
 // Wait (bounded, error word on timeout) until alpha * v of every rank is
@@ -559,7 +698,7 @@ __device__ __forceinline__ void alpha_v_operands(const DecodeParams& p, u32x4 (&
 __device__ __forceinline__ void b_fragments(const DecodeParams& p, int band,
                                             u32x4 (&bfr)[kRankSteps]) {
   const int lane = threadIdx.x & 63, wave = wave_id(), q = lane >> 4, c16 = lane & 15;
-  const int nrow = band * 64 + 16 * wave + c16;
+  const int nrow = band * BR + 16 * wave + c16;
   constexpr uint32_t kOut = 0x80000000u;
   const rsrc_t bs = make_rsrc(p.B, (uint32_t)p.N * p.r * 2);
   const uint32_t bro = (uint32_t)min(nrow, p.N - 1) * p.r * 2;
@@ -588,7 +727,7 @@ __device__ __forceinline__ void add_correction(const DecodeParams& p, const u32x
 template <int MT>
 __device__ __forceinline__ void store_row(const DecodeParams& p, int band, const f32x4 (&yv)[MT]) {
   const int lane = threadIdx.x & 63, wave = wave_id(), q = lane >> 4, c16 = lane & 15;
-  const int nrow = band * 64 + 16 * wave + c16;
+  const int nrow = band * BR + 16 * wave + c16;
   if (nrow < p.N)
     for (int mt = 0; mt < MT; ++mt)
       for (int i = 0; i < 4; ++i) {
@@ -599,90 +738,34 @@ __device__ __forceinline__ void store_row(const DecodeParams& p, int band, const
 
 // Add a partial sum to a band (slot sidx of nparts) and report whether this
 // workgroup arrived last; the last one gets the sum of all partials in slot
-// order in v and clears the band's counter.
+// order in v and clears the band's counter.  Waves with act false (those
+// past the 64 columns of a rank band) hold no column.
 template <int MT>
 __device__ __forceinline__ bool arrive(const DecodeParams& p, int band, int sidx, int nparts,
-                                       int* s_last, f32x4 (&v)[MT]) {
+                                       bool act, int* s_last, f32x4 (&v)[MT]) {
   const int tid = threadIdx.x, col = 16 * wave_id() + (tid & 15);
-  put_part<MT>(p, band, sidx, col, v);
+  if (act) put_part<MT>(p, band, sidx, col, v);
   wait_vmem();
   __syncthreads();
   if (tid == 0) *s_last = atomicAdd(&p.ctr[kCtrBand + band], 1) == nparts - 1;
   __syncthreads();
   const bool last = *s_last;
   if (last) {
-    sum_parts<MT>(p, band, nparts, col, v);
+    if (act) sum_parts<MT>(p, band, nparts, col, v);
     if (tid == 0) store_dev(&p.ctr[kCtrBand + band], 0);
   }
   return last;
 }
 
-// The correction workgroups: once the rank bands are published, alpha v B^T
-// of row bands wg, wg + cw, ... (kCorrBands / MT of them) goes in as each
-// band's extra partial (slot nseg); whoever arrives last at a band stores it.
-// All their B fragments are requested together, their partials stored
-// together, and one wait covers all the stores.  The finishers of the bands
-// from cw * kCorrBands / MT on add the correction themselves.
-template <int MT>
-__device__ void correction_partials(const DecodeParams& p, int wg, int* s_mask) {
-  constexpr int kCorrBatch = kCorrBands / MT;
-  const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
-  const int col = 16 * wave + (lane & 15);
-  // B does not depend on the rank bands: its fragments are requested first.
-  u32x4 bfr[kCorrBatch][kRankSteps];
-  for (int i = 0; i < kCorrBatch; ++i) b_fragments(p, min(wg + i * p.cw, p.NB - 1), bfr[i]);
-  wait_ranks(p);
-  u32x4 hi[kRankSteps][MT], lo[kRankSteps][MT];
-  alpha_v_operands<MT>(p, hi, lo);
-  {
-    const int nb0 = wg;
-    int nseg[kCorrBatch];
-    bool ok[kCorrBatch];
-    f32x4 v[kCorrBatch][MT];
-    for (int i = 0; i < kCorrBatch; ++i) {
-      const int nb = nb0 + i * p.cw, band = p.RB + nb;
-      const long long bbeg = (long long)band * p.KB, bend = bbeg + p.KB;
-      ok[i] = nb < p.NB;
-      nseg[i] = ok[i] ? owner_of(p, bend - 1) - owner_of(p, bbeg) + 1 : 0;
-      if (ok[i] && nseg[i] + 1 > p.maxseg) {  // cannot happen with a planner-sized workspace
-        if (tid == 0) atomicOr(&p.ctr[kCtrError], 2);
-        ok[i] = false;
-      }
-      for (int mt = 0; mt < MT; ++mt) v[i][mt] = f32x4{0.f, 0.f, 0.f, 0.f};
-      if (ok[i]) add_correction<MT>(p, bfr[i], hi, lo, v[i]);
-    }
-    for (int i = 0; i < kCorrBatch; ++i)
-      if (ok[i]) put_part<MT>(p, p.RB + nb0 + i * p.cw, nseg[i], col, v[i]);
-    wait_vmem();
-    __syncthreads();
-    if (wave == 0) {  // lane i counts band i in; the arrivals go out together
-      bool last = false;
-      if (lane < kCorrBatch) {
-        const int nb = nb0 + lane * p.cw, band = p.RB + nb;
-        const long long bbeg = (long long)band * p.KB, bend = bbeg + p.KB;
-        const int ns = nb < p.NB ? owner_of(p, bend - 1) - owner_of(p, bbeg) + 1 : 0;
-        if (nb < p.NB && ns + 1 <= p.maxseg)
-          last = atomicAdd(&p.ctr[kCtrBand + band], 1) == ns;
-      }
-      const uint64_t m = __ballot(last);
-      if (lane == 0) *s_mask = (int)(m & ((1u << kCorrBatch) - 1));
-    }
-    __syncthreads();
-    const int mask = *s_mask;
-    for (int i = 0; i < kCorrBatch; ++i)
-      if (mask & (1 << i)) {  // arrived last: every segment's partial is in
-        const int nb = nb0 + i * p.cw, band = p.RB + nb;
-        sum_parts<MT>(p, band, nseg[i] + 1, col, v[i]);
-        if (tid == 0) store_dev(&p.ctr[kCtrBand + band], 0);
-        store_row<MT>(p, nb, v[i]);
-      }
-  }
-}
-
+// Second bound: waves per SIMD (one workgroup of W waves per compute unit),
+// which gives a wave 256 registers: a burst's operands and both register
+// stages stay in registers.
 template <int MT, bool GROUPED>
-__global__ __launch_bounds__(256, 2) void decode_kernel(DecodeParams p) {
+__global__ __launch_bounds__(kThreads, W * kDecodeOccupancy / 4) void decode_kernel(DecodeParams p) {
+  // x buffers (also the MLP gate's working area, T (r + h) + max(r, h) floats)
+  static_assert(2 * Burst<MT>::kBuf / 4 >= 16 * MT * 256 + 128, "MLP gate LDS");
   __shared__ __attribute__((aligned(16))) uint8_t xlds[2 * Burst<MT>::kBuf];
-  __shared__ __attribute__((aligned(16))) uint8_t mlds[GROUPED ? 4 * kMetaWave : 16];
+  __shared__ __attribute__((aligned(16))) uint8_t mlds[GROUPED ? W * Meta<MT>::kWave : 16];
   __shared__ int s_last;
   const int tid = threadIdx.x;
   const int wg = blockIdx.x;
@@ -699,10 +782,7 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(DecodeParams p) {
     const int nseg = owner_of(p, bend - 1) - first + 1;
     const int sidx = wg - first;
     const bool rank = band < p.RB;
-    // a row band whose correction a correction workgroup adds takes one more
-    // partial
-    const bool corr = !rank && corrected<MT>(p, band - p.RB);
-    const int nparts = nseg + (corr ? 1 : 0);
+    const int nparts = nseg;
     if (nparts > p.maxseg) {  // cannot happen with a workspace sized by the planner
       if (tid == 0) atomicOr(&p.ctr[kCtrError], 2);
       continue;
@@ -712,7 +792,8 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(DecodeParams p) {
     if (rank) rank_segment<MT>(p, band, lo, hi, xlds, burst, v);
     else row_segment<MT, GROUPED>(p, band - p.RB, lo, hi, xlds, mlds, burst, v);
 
-    const bool fin = nparts == 1 || arrive<MT>(p, band, sidx, nparts, &s_last, v);
+    const bool fin = nparts == 1 || arrive<MT>(p, band, sidx, nparts, !rank || wave_id() < 4,
+                                               &s_last, v);
     if (fin) {
       if (rank) {
         finish_rank<MT>(p, band, v);
@@ -722,7 +803,7 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(DecodeParams p) {
         __syncthreads();
         if (p.gh > 0 && s_last) gate_mlp(p, xlds, 2 * Burst<MT>::kBuf / 4);
       } else {
-        if (p.r > 0 && !corr) {
+        if (p.r > 0) {
           u32x4 bfr[kRankSteps];
           b_fragments(p, band - p.RB, bfr);
           wait_ranks(p);
@@ -734,7 +815,6 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(DecodeParams p) {
       }
     }
   }
-  if (wg < p.cw) correction_partials<MT>(p, wg, &s_last);
 
   if (p.RB > 0 && tid == 0) {
     wait_vmem();
@@ -748,29 +828,29 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(DecodeParams p) {
 
 template <int MT, bool GROUPED>
 hipError_t go(const DecodeParams& p, hipStream_t st) {
-  hipLaunchKernelGGL((decode_kernel<MT, GROUPED>), dim3(p.P), dim3(256), 0, st, p);
+  hipLaunchKernelGGL((decode_kernel<MT, GROUPED>), dim3(p.P), dim3(kThreads), 0, st, p);
   return hipGetLastError();
 }
 
 }  // namespace
 
-// Workgroups the current device keeps resident: two per compute unit.
-static int resident_slots() {
+// Compute units of the current device.
+static int compute_units() {
   static int cached[64] = {0};
   int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 512;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
   if (cached[dev] == 0) {
     int cus = 0;
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
         cus <= 0)
       cus = 256;
-    cached[dev] = 2 * cus;
+    cached[dev] = cus;
   }
   return cached[dev];
 }
 
 hipError_t launch_decode(const Shape& s, const LayerArgs& a, const WsPtrs& w, hipStream_t st) {
-  const DecodePlan pl = plan_decode(s, resident_slots());
+  const DecodePlan pl = plan_decode(s, compute_units() * kDecodeOccupancy);
   DecodeParams p;
   p.x = static_cast<const uint16_t*>(a.x);
   p.wq = a.wq;
@@ -801,10 +881,10 @@ hipError_t launch_decode(const Shape& s, const LayerArgs& a, const WsPtrs& w, hi
   p.RB = pl.rank_bands;
   p.NB = pl.bands;
   p.P = pl.workgroups;
+  p.row_cost = pl.row_cost;
   p.rank_cost = pl.rank_cost;
   p.ctot = pl.cost;
   p.maxseg = pl.maxseg;
-  p.cw = pl.correction_wgs;
   if (s.T <= 16) return s.grouped ? go<1, true>(p, st) : go<1, false>(p, st);
   return s.grouped ? go<2, true>(p, st) : go<2, false>(p, st);
 }
