@@ -34,16 +34,18 @@ DecodePlan plan_decode(const Shape& s, int slots) {
   pl.rank_bands = (s.r + 63) / 64;
   pl.units = (pl.bands + pl.rank_bands) * KB;
   // Costs in KB moved: a row unit is kDecodeBandRows x 64 B of codes, a rank
-  // unit (ranks in the band) x 256 B of A, costed 1.25 times that so the rank
-  // bands, which every row finisher waits for, complete early.
-  const int ranks = std::min(std::max(s.r, 1), 64);
+  // unit 64 x 256 B of A, costed 1.25 times that so the rank bands, which
+  // every row finisher waits for, complete early.  A rank unit is costed as
+  // a full band whatever r is: its time (x, the barrier and four tiles of
+  // matrix-core work per block) hardly depends on how many ranks it holds.
   pl.row_cost = kDecodeBandRows / 16;
-  pl.rank_cost = std::max(1, (5 * ranks + 15) / 16);
+  pl.rank_cost = 20;
   pl.cost = (long long)pl.rank_bands * KB * pl.rank_cost + (long long)pl.bands * KB * pl.row_cost;
   // At least twice the dearest unit per workgroup: a run of cost C >= that
   // unit's cost always holds a unit, which the kernel's count of the
-  // workgroups sharing a band relies on.
-  const int umax = std::max(pl.row_cost, pl.rank_cost);
+  // workgroups sharing a band relies on (and a run whose start moves to an
+  // even block keeps one).
+  const int umax = pl.rank_bands > 0 ? std::max(pl.row_cost, pl.rank_cost) : pl.row_cost;
   auto wgs = [&](int sl) {
     long long P = std::min<long long>(sl, std::max<long long>(1, pl.cost / (2 * umax)));
     return (int)std::max<long long>(1, std::min<long long>(P, pl.units));

@@ -47,7 +47,7 @@ struct DecodePlan {
   int rank_bands;  // 64-rank bands of A
   int units;       // (bands + rank_bands) * K/128
   int row_cost;    // cost of one row unit (its KB of codes)
-  int rank_cost;   // cost of one rank unit (1.25 x its KB of A)
+  int rank_cost;   // cost of one rank unit (1.25 x the KB of a full 64-rank band)
   long long cost;  // total cost of all units
   int workgroups;  // persistent workgroups, each a run of units of equal cost
   int maxseg;      // bound on the partial sums of one band (any P up to kMaxSlots): the

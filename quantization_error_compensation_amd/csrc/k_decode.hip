@@ -103,13 +103,13 @@ struct Burst {
 
 // ------------------------------------------------------------- partition
 // Cost of the first u units, and the first unit of workgroup w: the smallest
-// u with S(u) * P >= w * ctot.  owner_of(u) is the workgroup whose run holds
-// unit u.
+// u with S(u) * P >= w * ctot (moved to an even block of a row band).
+// owner_of(u) is the workgroup whose run holds unit u.
 __device__ __forceinline__ long long cost_prefix(const DecodeParams& p, long long u) {
   const long long ru = (long long)p.RB * p.KB;
   return u <= ru ? u * p.rank_cost : ru * p.rank_cost + (u - ru) * p.row_cost;
 }
-__device__ __forceinline__ long long unit_begin(const DecodeParams& p, int w) {
+__device__ __forceinline__ long long unit_begin_exact(const DecodeParams& p, int w) {
   const long long X = (long long)w * p.ctot;
   const long long ru = (long long)p.RB * p.KB;
   const long long rc = (long long)p.rank_cost * p.P;
@@ -117,8 +117,18 @@ __device__ __forceinline__ long long unit_begin(const DecodeParams& p, int w) {
   if (X <= ru * rc) return (X + rc - 1) / rc;
   return ru + (X - ru * rc + wc - 1) / wc;
 }
+// Runs start at an even block of a row band, so the bursts' code loads stay
+// aligned to 128-byte lines: a start at an odd offset moves one unit on (a
+// run keeps at least one unit, since it costs at least two of the dearest).
+__device__ __forceinline__ long long unit_begin(const DecodeParams& p, int w) {
+  long long u = unit_begin_exact(p, w);
+  const long long ru = (long long)p.RB * p.KB;
+  if (u > ru && u < ru + (long long)p.NB * p.KB && ((u - ru) % p.KB) % 2 == 1) ++u;
+  return u;
+}
 __device__ __forceinline__ int owner_of(const DecodeParams& p, long long u) {
-  return (int)(cost_prefix(p, u) * p.P / p.ctot);
+  const int o = (int)(cost_prefix(p, u) * p.P / p.ctot);
+  return u == unit_begin_exact(p, o) && unit_begin(p, o) != u ? o - 1 : o;  // moved start
 }
 
 // ------------------------------------------------------------- x staging
