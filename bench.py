@@ -42,10 +42,11 @@ HBM_PEAK_GBS = 8000.0
 BF16_PEAK_TFLOPS = 2500.0
 
 
-def layer_bytes(K, N, r, g, asym, T):
+def layer_bytes(K, N, r, g, asym, T, serq=False):
     G = K // g
     w = N * K // 2 + N * G * 2 + (N * ((G + 7) // 8) * 4 if asym else 0)
-    comp = r * K * 2 + N * r * 2 + 2 * r * 4
+    # SPEAR: A, B, g, b; SERQ: R only (its k salient channels come from x)
+    comp = N * r * 2 if serq else r * K * 2 + N * r * 2 + 2 * r * 4
     return w + comp + T * K * 2 + T * N * 2
 
 
@@ -54,7 +55,9 @@ def weight_bytes(K, N, r, g, asym):
     return N * K // 2 + N * G * 2 + (N * ((G + 7) // 8) * 4 if asym else 0) + r * K * 2 + N * r * 2
 
 
-def layer_flops(K, N, r, T):
+def layer_flops(K, N, r, T, serq=False):
+    if serq:  # W4 product + the k-channel reconstruction
+        return 2 * T * K * N + 2 * T * r * N
     return 2 * T * K * N + 2 * T * r * (K + N) + 4 * T * r
 
 
@@ -96,6 +99,9 @@ def parse():
     ap.add_argument("--rank", type=int, default=None, help="override the compensator rank")
     ap.add_argument("--mlp-gate", type=int, default=0, metavar="H",
                     help="use the bottleneck-MLP gate of width H (0: the elementwise gate)")
+    ap.add_argument("--serq", type=int, default=0, metavar="K",
+                    help="SERQ single-matrix reconstruction of K salient channels (the first K "
+                         "after the permutation) instead of the SPEAR compensator")
     ap.add_argument("--copies", type=int, default=0, help="weight copies to rotate (0 = auto)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -134,14 +140,19 @@ def main():
     spec = synth.CONFIGS[args.config]
     K, N, g, asym = spec.d_in, spec.d_out, spec.group_size, spec.asym
     r = spec.rank if args.rank is None else args.rank
+    serq = args.serq > 0
+    if serq:
+        r = args.serq
     plan = WORKLOADS[args.config]["steps"]
     Tmax = max(T for _, T in plan)
     Ttot = sum(T for _, T in plan)
 
     t_setup = time.time()
     W = synth.weights(spec)
-    X = synth.activations(spec, Ttot)
+    X = synth.serq_activations(spec, Ttot) if serq else synth.activations(spec, Ttot)
     A, B, gv, bv = synth.compensator(spec, r)
+    if serq:  # R in B's place; no A, g, b
+        B = synth.serq_matrix(spec, r)
     mlp = synth.mlp_gate(spec, r, args.mlp_gate) if args.mlp_gate and r else None
     desc = q.make_desc(K, N, r, g, asym, spec.per_tensor)
     wq0, sc0, zs0 = q.alloc_packed(desc, dev)
@@ -173,7 +184,10 @@ def main():
         for j, (path, T) in enumerate(plan):
             if evs is not None:
                 evs[j].record(stream)
-            if L["mlp"] is not None:
+            if serq:
+                q.spear_ec_linear_serq(desc, xs[j], L["wq"], L["sc"], L["zs"], 0, L["B"], ys[j],
+                                       ws, stream)
+            elif L["mlp"] is not None:
                 m = L["mlp"]
                 q.spear_ec_linear_mlp_gate(desc, xs[j], L["wq"], L["sc"], L["zs"], L["A"], L["B"],
                                            m["w1"], m["b1"], m["w2"], m["b2"], spec.alpha, ys[j],
@@ -205,8 +219,8 @@ def main():
 
     calls = []
     for j, (path, T) in enumerate(plan):
-        by = layer_bytes(K, N, r, g, asym, T)
-        fl = layer_flops(K, N, r, T)
+        by = layer_bytes(K, N, r, g, asym, T, serq)
+        fl = layer_flops(K, N, r, T, serq)
         s = per_call_ms[j] / 1e3
         calls.append(dict(path=path, tokens=T, ms=per_call_ms[j], bytes=by, flops=fl,
                           gbs=by / s / 1e9, tflops=fl / s / 1e12))
@@ -220,7 +234,8 @@ def main():
     dec = [c for c in calls if c["path"] == "decode"]
     pre = [c for c in calls if c["path"] == "prefill"]
     dominant = max(calls, key=lambda c: c["ms"])
-    traffic = load_traffic(args.config)
+    # the stored counter figures are for the default elementwise-gate layer
+    traffic = {} if (serq or mlp) else load_traffic(args.config)
 
     def roof(c):
         if c["path"] == "decode":
@@ -247,7 +262,8 @@ def main():
         "config": {"workload": f"{args.config}: " + WORKLOADS[args.config]["text"],
                    "d_in": K, "d_out": N, "rank": r, "group_size": g,
                    "zero_points": asym, "per_tensor": spec.per_tensor,
-                   "gate": f"bottleneck MLP, hidden {args.mlp_gate}" if mlp else "elementwise",
+                   "gate": (f"SERQ, {r} salient channels" if serq else
+                            f"bottleneck MLP, hidden {args.mlp_gate}" if mlp else "elementwise"),
                    "tokens_per_step": [T for _, T in plan],
                    "weight_copies_rotated": copies, "parallelism": "single GPU"},
         "calls": [{k: (round(v, 4) if isinstance(v, float) else v) for k, v in c.items()}
@@ -262,7 +278,7 @@ def main():
     out["setup_s"] = round(setup_s, 1)
 
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(spec, r, plan, X, A, B, gv, bv, unit, mlp)
+        out["cpu_baseline"] = cpu_baseline(spec, r, plan, X, A, B, gv, bv, unit, mlp, serq)
     print(json.dumps(out), flush=True)
 
 
@@ -337,7 +353,7 @@ def load_traffic(config):
     return t.get("bytes_per_call", {})
 
 
-def cpu_baseline(spec, r, plan, X, A, B, gv, bv, unit, mlp=None):
+def cpu_baseline(spec, r, plan, X, A, B, gv, bv, unit, mlp=None, serq=False):
     """The fp64 oracle on a bounded sample of the same layer: every token of
     the first call of the step, a slice of output rows.  Scaled to the unit
     of `value` by the algorithmic bytes (or flops) of that slice."""
@@ -352,12 +368,15 @@ def cpu_baseline(spec, r, plan, X, A, B, gv, bv, unit, mlp=None):
     t0 = time.time()
     wq, sc, zs = oracle.quantize_rtn_per_tensor(Wsl) if spec.per_tensor else oracle.quantize_rtn(Wsl, g, asym)
     t1 = time.time()
-    oracle.forward(x, wq, sc, zs, A if r else None, B[:rows] if r else None, gv, bv, spec.alpha, g,
-                   mlp=mlp)
+    if serq:
+        oracle.forward_serq(x, wq, sc, zs, 0, B[:rows], g)
+    else:
+        oracle.forward(x, wq, sc, zs, A if r else None, B[:rows] if r else None, gv, bv,
+                       spec.alpha, g, mlp=mlp)
     t2 = time.time()
     secs = t2 - t1
-    by = layer_bytes(K, rows, r, g, asym, T)
-    fl = layer_flops(K, rows, r, T)
+    by = layer_bytes(K, rows, r, g, asym, T, serq)
+    fl = layer_flops(K, rows, r, T, serq)
     val = by / secs / 1e9 if unit == "GB/s" else fl / secs / 1e12
     return {"value": round(val, 6), "unit": unit, "cores": 1, "kind": "oracle",
             "sample": f"{path} call, all {T} tokens x first {rows} of {N} output rows "

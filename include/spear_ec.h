@@ -93,7 +93,8 @@ typedef struct spear_ec_desc {
 
 /*
  * Bytes of scratch device memory one call with up to `max_tokens` tokens
- * needs (either path).  The workspace holds the rank-r projections, per-block
+ * needs (either path, and spear_ec_linear_serq).  The workspace holds the
+ * rank-r projections, per-block
  * sums of x, split-K partial sums and a few arrival counters.  Its first use
  * requires it to be zero-filled by the caller (hipMemset once after
  * allocation); every call leaves the counters at zero again.  One workspace
@@ -159,6 +160,25 @@ int spear_ec_linear_mlp_gate(const spear_ec_desc* desc, int32_t tokens, const vo
                              const float* b1, const float* w2, const float* b2, float alpha,
                              void* y, void* workspace, size_t workspace_bytes,
                              hipStream_t stream);
+
+/*
+ * SERQ single-matrix reconstruction ("SERQ: Saliency-Aware Low-Rank Error
+ * Reconstruction for LLM Quantization", section 2 on the single matrix and the
+ * offline permutation): the salient input channels, contiguous after the
+ * offline permutation, are x[:, s0 .. s0 + k) with s0 = salient_begin and
+ * k = desc.rank; one matrix R reconstructs their quantization error,
+ *     y[t, n] = sum_k W~[n, k] x[t, k] + sum_{j<k} R[n, j] x[t, s0 + j],
+ * with no projection, no gate and no intermediate quantization.  R is bf16
+ * [d_out][k] (row n holds output n's k weights, B's layout); x, wq, scales,
+ * zeros, y, workspace and the token-count dispatch are as for
+ * spear_ec_linear.  Requires k > 0 (a multiple of 16 up to 128), salient_begin
+ * a multiple of 8 and salient_begin + k <= d_in, else
+ * SPEAR_EC_ERR_INVALID_ARGUMENT / SPEAR_EC_ERR_UNSUPPORTED.
+ */
+int spear_ec_linear_serq(const spear_ec_desc* desc, int32_t tokens, const void* x,
+                         const uint32_t* wq, const void* scales, const uint32_t* zeros,
+                         int32_t salient_begin, const void* R, void* y, void* workspace,
+                         size_t workspace_bytes, hipStream_t stream);
 
 /*
  * Round-to-nearest int4 quantization of fp32 weights w [d_out][d_in] into the

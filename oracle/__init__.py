@@ -6,9 +6,10 @@ arithmetic lives in ``spear_oracle.cpp`` (single-threaded C++, double
 precision); this module only loads that library and marshals numpy arrays.
 
 What each function follows is stated in the C++ file: the RTN quantizer
-(SPEAR summary, section 3.1, RTN per-channel setting), the dequantization, and
-the compensated product with the effective weight
-W~ + alpha * B * diag(gamma(A x)) * A (SPEAR summary, section 2.1 A).
+(SPEAR summary, section 3.1, RTN per-channel setting), the dequantization, the
+compensated product with the effective weight
+W~ + alpha * B * diag(gamma(A x)) * A (SPEAR summary, section 2.1 A), and
+SERQ's single-matrix reconstruction W~ x + R x[S] (SERQ summary, section 2).
 """
 from __future__ import annotations
 
@@ -69,6 +70,11 @@ def _load():
         lib.orc_forward_sampled.restype = None
         lib.orc_forward_effective_weight.argtypes = fwd + [P]
         lib.orc_forward_effective_weight.restype = None
+        serq = [i32, i32, i32, i32, i32, P, P, P, P, i32, P]
+        lib.orc_forward_serq.argtypes = serq + [P]
+        lib.orc_forward_serq.restype = None
+        lib.orc_forward_serq_sampled.argtypes = serq + [i32, P, P, P]
+        lib.orc_forward_serq_sampled.restype = None
         lib.orc_set_mlp_gate.argtypes = [i32, P, P, P, P]
         lib.orc_set_mlp_gate.restype = None
         _lib = lib
@@ -238,4 +244,37 @@ def forward_effective_weight(x, wq, scales, zeros, A, B, g, b, alpha, group_size
         _load().orc_forward_effective_weight(T, K, N, r, group_size, _p(x), _p(wq), _p(sc),
                                              _p(zs), _p(A), _p(B), _p(g), _p(b), float(alpha),
                                              _p(y))
+    return y
+
+
+def _serq_args(x, wq, scales, zeros, s0, R):
+    x = _c(x, np.uint16)
+    wq = _c(wq, np.uint32)
+    sc = _c(scales, np.uint16)
+    zs = None if zeros is None else _c(zeros, np.uint32)
+    R = _c(R, np.uint16)
+    T, K = x.shape
+    N, k = R.shape
+    if not (0 <= s0 and s0 + k <= K):
+        raise ValueError("salient channels out of range")
+    return x, wq, sc, zs, R, T, K, N, k
+
+
+def forward_serq(x, wq, scales, zeros, s0, R, group_size):
+    """y (double [T][N]) of SERQ's single-matrix reconstruction:
+    W~ x + R x[:, s0 : s0 + k]; x, R (d_out x k) are bf16 bit arrays."""
+    x, wq, sc, zs, R, T, K, N, k = _serq_args(x, wq, scales, zeros, s0, R)
+    y = np.empty((T, N), np.float64)
+    _load().orc_forward_serq(T, K, N, k, group_size, _p(x), _p(wq), _p(sc), _p(zs), int(s0),
+                             _p(R), _p(y))
+    return y
+
+
+def forward_serq_sampled(x, wq, scales, zeros, s0, R, group_size, t_idx, n_idx):
+    x, wq, sc, zs, R, T, K, N, k = _serq_args(x, wq, scales, zeros, s0, R)
+    ti = _c(t_idx, np.int32)
+    ni = _c(n_idx, np.int32)
+    y = np.empty(ti.size, np.float64)
+    _load().orc_forward_serq_sampled(T, K, N, k, group_size, _p(x), _p(wq), _p(sc), _p(zs),
+                                     int(s0), _p(R), int(ti.size), _p(ti), _p(ni), _p(y))
     return y

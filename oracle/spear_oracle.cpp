@@ -17,6 +17,8 @@
 //     symmetric per-tensor scale of the Quasar verify pass (Quasar summary,
 //     "Targeted quantization": one symmetric scaling factor per tensor).
 //   * Unpack / dequantization of the packed codes:  W~[n,k] = (c - z) * s.
+//   * SERQ's single-matrix reconstruction of the salient channels' error
+//     (SERQ summary, section 2), orc_forward_serq.
 //   * The compensated product (SPEAR summary, section 2.1 A, input-adaptive
 //     error compensators): the effective weight for token x is
 //         W~ + alpha * B * diag(gamma(A x)) * A,
@@ -387,6 +389,50 @@ void orc_forward_effective_weight(int T, int K, int N, int r, int g,
       for (int k = 0; k < K; ++k) acc += Weff[(size_t)n * K + k] * xt[k];
       y[(size_t)t * N + n] = acc;
     }
+  }
+}
+
+// SERQ single-matrix reconstruction ("SERQ: Saliency-Aware Low-Rank Error
+// Reconstruction for LLM Quantization", section 2: salient channels chosen by
+// activation scale, contiguous after the offline permutation; one matrix R
+// reconstructs their quantization error, with no intermediate quantization):
+//   y[t,n] = sum_k W~[n,k] x[t,k] + sum_{j<k} R[n,j] x[t, s0 + j].
+// R: bf16 bits [N][k].  y: double [T][N].
+void orc_forward_serq(int T, int K, int N, int k, int g, const uint16_t* x,
+                      const uint32_t* wq, const uint16_t* scales, const uint32_t* zeros,
+                      int s0, const uint16_t* R, double* y) {
+  std::vector<double> xd((size_t)T * K), w(K);
+  for (size_t i = 0; i < (size_t)T * K; ++i) xd[i] = orc_bf16_to_double(x[i]);
+  for (int n = 0; n < N; ++n) {
+    dequant_row(wq, scales, zeros, K, g, n, w.data());
+    for (int t = 0; t < T; ++t) {
+      const double* xt = &xd[(size_t)t * K];
+      double acc = 0.0;
+      for (int c = 0; c < K; ++c) acc += w[c] * xt[c];
+      double corr = 0.0;
+      for (int j = 0; j < k; ++j) corr += orc_bf16_to_double(R[(size_t)n * k + j]) * xt[s0 + j];
+      y[(size_t)t * N + n] = acc + corr;
+    }
+  }
+}
+
+// Same quantity at a list of (t, n) positions only.
+void orc_forward_serq_sampled(int T, int K, int N, int k, int g, const uint16_t* x,
+                              const uint32_t* wq, const uint16_t* scales,
+                              const uint32_t* zeros, int s0, const uint16_t* R, int count,
+                              const int32_t* t_idx, const int32_t* n_idx, double* y) {
+  (void)T;
+  (void)N;
+  std::vector<double> xt(K), w(K);
+  for (int i = 0; i < count; ++i) {
+    const int t = t_idx[i], n = n_idx[i];
+    for (int c = 0; c < K; ++c) xt[c] = orc_bf16_to_double(x[(size_t)t * K + c]);
+    dequant_row(wq, scales, zeros, K, g, n, w.data());
+    double acc = 0.0;
+    for (int c = 0; c < K; ++c) acc += w[c] * xt[c];
+    double corr = 0.0;
+    for (int j = 0; j < k; ++j) corr += orc_bf16_to_double(R[(size_t)n * k + j]) * xt[s0 + j];
+    y[i] = acc + corr;
   }
 }
 

@@ -27,7 +27,8 @@ SPEAR_EC_DECODE_MAX_TOKENS = 32
 
 EXPORTED = (
     "spear_ec_workspace_bytes", "spear_ec_linear", "spear_ec_linear_decode",
-    "spear_ec_linear_prefill", "spear_ec_linear_mlp_gate", "spear_ec_quantize_rtn",
+    "spear_ec_linear_prefill", "spear_ec_linear_mlp_gate", "spear_ec_linear_serq",
+    "spear_ec_quantize_rtn",
     "spear_ec_dequant_f32", "spear_ec_status_string", "spear_ec_last_error", "spear_ec_version",
 )
 
@@ -66,6 +67,8 @@ def load_library(path: str = LIB_PATH):
     lib.spear_ec_linear_mlp_gate.argtypes = [DP, i32, P, P, P, P, P, P, i32, P, P, P, P,
                                              ctypes.c_float, P, P, sz, P]
     lib.spear_ec_linear_mlp_gate.restype = ctypes.c_int
+    lib.spear_ec_linear_serq.argtypes = [DP, i32, P, P, P, P, i32, P, P, P, sz, P]
+    lib.spear_ec_linear_serq.restype = ctypes.c_int
     lib.spear_ec_quantize_rtn.argtypes = [DP, P, P, P, P, P]
     lib.spear_ec_quantize_rtn.restype = ctypes.c_int
     lib.spear_ec_dequant_f32.argtypes = [DP, P, P, P, P, P]
@@ -163,6 +166,17 @@ def spear_ec_linear_mlp_gate(desc, x, wq, scales, zeros, A, B, w1, b1, w2, b2, a
         ctypes.byref(desc), tokens, _ptr(x), _ptr(wq), _ptr(scales), _ptr(zeros), _ptr(A),
         _ptr(B), hidden, _ptr(w1), _ptr(b1), _ptr(w2), _ptr(b2), float(alpha), _ptr(y),
         _ptr(workspace), ws_bytes, _stream(stream)))
+
+
+def spear_ec_linear_serq(desc, x, wq, scales, zeros, salient_begin, R, y, workspace,
+                         stream=None):
+    """SERQ single-matrix reconstruction: y = W~ x + R x[:, s0 : s0 + k]
+    (k = desc.rank, R bf16 [d_out][k])."""
+    tokens = int(x.shape[0])
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check(load_library().spear_ec_linear_serq(
+        ctypes.byref(desc), tokens, _ptr(x), _ptr(wq), _ptr(scales), _ptr(zeros),
+        int(salient_begin), _ptr(R), _ptr(y), _ptr(workspace), ws_bytes, _stream(stream)))
 
 
 def spear_ec_quantize_rtn(desc, w, wq, scales, zeros, stream=None):

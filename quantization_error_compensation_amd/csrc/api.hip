@@ -31,7 +31,7 @@ DecodePlan plan_decode(const Shape& s, int slots) {
   DecodePlan pl;
   const int KB = s.KB();
   pl.bands = (s.N + kDecodeBandRows - 1) / kDecodeBandRows;
-  pl.rank_bands = (s.r + 63) / 64;
+  pl.rank_bands = s.serq ? 0 : (s.r + 63) / 64;  // SERQ takes x's channels, no projection
   pl.units = (pl.bands + pl.rank_bands) * KB;
   // Costs in KB moved: a row unit is kDecodeBandRows x 64 B of codes, a rank
   // unit 64 x 256 B of A, costed 1.25 times that so the rank bands, which
@@ -158,8 +158,9 @@ static int check_desc(const spear_ec_desc* d, bool need_rank) {
   return SPEAR_EC_OK;
 }
 
-static Shape make_shape(const spear_ec_desc* d, int T) {
+static Shape make_shape(const spear_ec_desc* d, int T, bool serq = false) {
   Shape s;
+  s.serq = serq;
   s.K = d->d_in;
   s.N = d->d_out;
   s.r = d->rank;
@@ -241,6 +242,59 @@ static int linear(Path path, const spear_ec_desc* d, int32_t tokens, const void*
   return hip_status(launch_prefill(s, a, wp, stream), "prefill kernel launch");
 }
 
+// SERQ single-matrix reconstruction through the same kernels: decode with no
+// rank bands (each band's finisher adds x[:, S] R^T), prefill with the block
+// sums of x from the projection kernel at rank 0, the salient channels copied
+// as the epilogue operand, then the GEMM with R in B's place.
+static int linear_serq(const spear_ec_desc* d, int32_t tokens, const void* x, const uint32_t* wq,
+                       const void* scales, const uint32_t* zeros, int32_t s0, const void* R,
+                       void* y, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  g_last_error[0] = 0;
+  int rc = check_desc(d, true);
+  if (rc) return rc;
+  if (d->rank <= 0) return fail(SPEAR_EC_ERR_UNSUPPORTED, "SERQ needs rank (salient channels) > 0");
+  if (s0 < 0 || s0 % 8 != 0 || s0 > d->d_in - d->rank)
+    return fail(SPEAR_EC_ERR_INVALID_ARGUMENT,
+                "salient_begin must be a multiple of 8 with salient_begin + rank <= d_in");
+  if (tokens < 0) return fail(SPEAR_EC_ERR_INVALID_ARGUMENT, "tokens is negative");
+  if (tokens > 65536) return fail(SPEAR_EC_ERR_UNSUPPORTED, "tokens must be at most 65536");
+  if (tokens == 0) return SPEAR_EC_OK;
+  const bool has_z = (d->flags & SPEAR_EC_ZEROS) != 0;
+  if (!x || !wq || !scales || !y || !R)
+    return fail(SPEAR_EC_ERR_INVALID_ARGUMENT, "x, wq, scales, R and y are required");
+  if (has_z && !zeros) return fail(SPEAR_EC_ERR_INVALID_ARGUMENT, "zeros is required with SPEAR_EC_ZEROS");
+  if (!workspace) return fail(SPEAR_EC_ERR_WORKSPACE, "workspace is NULL");
+  const void* ptrs[] = {x, wq, scales, y, workspace, R, has_z ? zeros : nullptr};
+  for (const void* p : ptrs)
+    if (p && !aligned16(p)) return fail(SPEAR_EC_ERR_MISALIGNED, "a pointer is not 16-byte aligned");
+  const bool decode = tokens <= SPEAR_EC_DECODE_MAX_TOKENS;
+  const Shape s = make_shape(d, tokens, true);
+  const Workspace wl = layout(s, decode);
+  if (workspace_bytes < wl.total) return fail(SPEAR_EC_ERR_WORKSPACE, "workspace is smaller than spear_ec_workspace_bytes()");
+  LayerArgs a;
+  a.x = x;
+  a.wq = wq;
+  a.scales = static_cast<const uint16_t*>(scales);
+  a.zeros = has_z ? zeros : nullptr;
+  a.A = nullptr;
+  a.B = R;
+  a.gv = a.bv = nullptr;
+  a.gh = 0;
+  a.w1 = a.b1 = a.w2 = a.b2 = nullptr;
+  a.alpha = 1.f;
+  a.y = y;
+  a.s0 = s0;
+  const WsPtrs wp = carve(workspace, wl);
+  if (decode) return hip_status(launch_decode(s, a, wp, stream), "decode kernel launch");
+  Shape s_sums = s;  // the block sums of x only
+  s_sums.r = 0;
+  rc = hip_status(launch_projection(s_sums, a, wp, stream), "projection kernel launch");
+  if (rc) return rc;
+  rc = hip_status(launch_serq_operand(s, a, wp, stream), "SERQ operand launch");
+  if (rc) return rc;
+  return hip_status(launch_prefill(s, a, wp, stream), "prefill kernel launch");
+}
+
 }  // namespace spear
 
 using namespace spear;
@@ -251,12 +305,16 @@ size_t spear_ec_workspace_bytes(const spear_ec_desc* desc, int32_t max_tokens) {
   if (check_desc(desc, true) != SPEAR_EC_OK || max_tokens < 0 || max_tokens > 65536) return 0;
   size_t need = 0;
   const int td = std::min<int32_t>(max_tokens, SPEAR_EC_DECODE_MAX_TOKENS);
-  // Region sizes grow with the token count, so the largest count of each path bounds it.
+  // Region sizes grow with the token count, so the largest count of each
+  // path bounds it; SERQ calls (rank > 0) have their own decode plan.
   for (int t : {td, (int)max_tokens}) {
     if (t <= 0) continue;
-    const Shape s = make_shape(desc, t);
-    need = std::max(need, layout(s, false).total);
-    if (t <= SPEAR_EC_DECODE_MAX_TOKENS) need = std::max(need, layout(s, true).total);
+    for (bool serq : {false, true}) {
+      if (serq && desc->rank == 0) continue;
+      const Shape s = make_shape(desc, t, serq);
+      need = std::max(need, layout(s, false).total);
+      if (t <= SPEAR_EC_DECODE_MAX_TOKENS) need = std::max(need, layout(s, true).total);
+    }
   }
   if (need == 0) need = layout(make_shape(desc, 1), false).total;
   return need;
@@ -300,6 +358,14 @@ int spear_ec_linear_mlp_gate(const spear_ec_desc* desc, int32_t tokens, const vo
   }
   return linear(kAuto, desc, tokens, x, wq, scales, zeros, A, B, nullptr, nullptr, alpha, y,
                 workspace, workspace_bytes, stream, MlpGate{hidden, w1, b1, w2, b2});
+}
+
+int spear_ec_linear_serq(const spear_ec_desc* desc, int32_t tokens, const void* x,
+                         const uint32_t* wq, const void* scales, const uint32_t* zeros,
+                         int32_t salient_begin, const void* R, void* y, void* workspace,
+                         size_t workspace_bytes, hipStream_t stream) {
+  return linear_serq(desc, tokens, x, wq, scales, zeros, salient_begin, R, y, workspace,
+                     workspace_bytes, stream);
 }
 
 int spear_ec_quantize_rtn(const spear_ec_desc* desc, const float* w, uint32_t* wq, void* scales,

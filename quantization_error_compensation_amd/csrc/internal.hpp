@@ -32,6 +32,7 @@ struct Shape {
   int K, N, r, g, T;
   bool grouped;  // g == 128 (per-group scales); otherwise g == K
   bool zeros;
+  bool serq = false;  // SERQ call: r salient channels of x, no projection (no rank bands)
   int KB() const { return K / kBlockK; }
 };
 
@@ -104,12 +105,16 @@ struct LayerArgs {
   const float* b2;
   float alpha;
   void* y;
+  // SERQ (s0 >= 0): the correction is x[:, s0 .. s0 + r) R^T with R in B's
+  // place (no A, no gate, alpha 1)
+  int s0 = -1;
 };
 
 hipError_t launch_projection(const Shape& s, const LayerArgs& a, const WsPtrs& w,
                              hipStream_t st);
 hipError_t launch_decode(const Shape& s, const LayerArgs& a, const WsPtrs& w, hipStream_t st);
 hipError_t launch_prefill(const Shape& s, const LayerArgs& a, const WsPtrs& w, hipStream_t st);
+hipError_t launch_serq_operand(const Shape& s, const LayerArgs& a, const WsPtrs& w, hipStream_t st);
 hipError_t launch_quantize(int N, int K, int g, bool asym, bool per_tensor, const float* w,
                            uint32_t* wq, uint16_t* scales, uint32_t* zeros, hipStream_t st);
 hipError_t launch_dequant(int N, int K, int g, const uint32_t* wq, const uint16_t* scales,

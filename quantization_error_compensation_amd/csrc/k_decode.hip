@@ -76,6 +76,8 @@ struct DecodeParams {
   int row_cost;            // cost of a row unit
   int rank_cost;           // cost of a rank unit
   long long ctot;          // total cost of all units
+  int s0;                  // SERQ: first salient channel (the correction is x[:, s0 ..] R^T,
+                           // R in B's place, no rank bands); -1 otherwise
   int maxseg;              // bound on the partial sums of one band
 };
 
@@ -703,6 +705,23 @@ __device__ __forceinline__ void alpha_v_operands(const DecodeParams& p, u32x4 (&
     }
 }
 
+// SERQ's operands: the salient channels x[t, s0 + 32 k + 8 q ..] of this
+// lane's tokens, already bf16 (SERQ summary: one extra product with the
+// salient activations, no intermediate quantization).
+template <int MT>
+__device__ __forceinline__ void serq_operands(const DecodeParams& p, u32x4 (&hi)[kRankSteps][MT]) {
+  const int lane = threadIdx.x & 63, q = lane >> 4, c16 = lane & 15;
+  constexpr uint32_t kOut = 0x80000000u;
+  const rsrc_t xr = make_rsrc(p.x, (uint32_t)p.T * p.K * 2);
+  for (int k = 0; k < kRankSteps; ++k) {
+    const int jj = 32 * k + 8 * q;
+    for (int mt = 0; mt < MT; ++mt) {
+      const int t = 16 * mt + c16;
+      hi[k][mt] = bload16(xr, jj < p.r && t < p.T ? (uint32_t)(t * p.K + p.s0 + jj) * 2 : kOut, 0);
+    }
+  }
+}
+
 // B fragments of the 16 rows of this wave's tile of a row band: for each
 // K = 32 rank step, 8 ranks of the lane's row (zero past r).
 __device__ __forceinline__ void b_fragments(const DecodeParams& p, int band,
@@ -816,9 +835,15 @@ __global__ __launch_bounds__(kThreads, W * kDecodeOccupancy / 4) void decode_ker
         if (p.r > 0) {
           u32x4 bfr[kRankSteps];
           b_fragments(p, band - p.RB, bfr);
-          wait_ranks(p);
           u32x4 vhi[kRankSteps][MT], vlo[kRankSteps][MT];
-          alpha_v_operands<MT>(p, vhi, vlo);
+          if (p.s0 >= 0) {  // SERQ: x's salient channels, nothing to wait for
+            serq_operands<MT>(p, vhi);
+            for (int k = 0; k < kRankSteps; ++k)
+              for (int mt = 0; mt < MT; ++mt) vlo[k][mt] = u32x4{0u, 0u, 0u, 0u};
+          } else {
+            wait_ranks(p);
+            alpha_v_operands<MT>(p, vhi, vlo);
+          }
           add_correction<MT>(p, bfr, vhi, vlo, v);
         }
         store_row<MT>(p, band - p.RB, v);
@@ -895,6 +920,7 @@ hipError_t launch_decode(const Shape& s, const LayerArgs& a, const WsPtrs& w, hi
   p.rank_cost = pl.rank_cost;
   p.ctot = pl.cost;
   p.maxseg = pl.maxseg;
+  p.s0 = a.s0;
   if (s.T <= 16) return s.grouped ? go<1, true>(p, st) : go<1, false>(p, st);
   return s.grouped ? go<2, true>(p, st) : go<2, false>(p, st);
 }

@@ -191,6 +191,26 @@ __global__ __launch_bounds__(128) void finish_mlp_kernel(ProjParams p) {
 
 }  // namespace
 
+// SERQ's correction operand for the prefill epilogue (SERQ summary: one extra
+// product with the salient activations, no intermediate quantization):
+// wvhi[t][j] = x[t][s0 + j] (already bf16), wvlo = 0.
+__global__ __launch_bounds__(256) void serq_operand_kernel(const uint16_t* x, int K, int s0, int T,
+                                                           int r, uint16_t* wvhi, uint16_t* wvlo) {
+  const int e = blockIdx.x * 256 + threadIdx.x;
+  if (e >= T * r) return;
+  const int t = e / r, j = e - t * r;
+  wvhi[e] = x[(size_t)t * K + s0 + j];
+  wvlo[e] = 0;
+}
+
+hipError_t launch_serq_operand(const Shape& s, const LayerArgs& a, const WsPtrs& w,
+                               hipStream_t st) {
+  const int elems = s.T * s.r;
+  hipLaunchKernelGGL(serq_operand_kernel, dim3((elems + 255) / 256), dim3(256), 0, st,
+                     static_cast<const uint16_t*>(a.x), s.K, a.s0, s.T, s.r, w.wvhi, w.wvlo);
+  return hipGetLastError();
+}
+
 hipError_t launch_projection(const Shape& s, const LayerArgs& a, const WsPtrs& w,
                              hipStream_t st) {
   const ProjPlan pl = plan_projection(s);

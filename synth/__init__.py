@@ -24,7 +24,7 @@ x ~ N(0, 1) with a fixed set of round_half_up(frac * d_in) outlier channels
 (frac 1%, factor 20; c2: 0.5%, 30) multiplied in fp64 and rounded once,
 directly, to bf16; A ~ N(0, variance 1/d_in); B ~ N(0, 0.01); g ~ N(1, 0.1)
 (fp32); b = 0; alpha = 1.  Seeds: 1000 * config + tensor id
-(W 1, x 2, outlier set 3, A 4, B 5, g 6, b 7).
+(W 1, x 2, outlier set 3, A 4, B 5, g 6, b 7, MLP gate 8-11, SERQ's R 12).
 """
 from __future__ import annotations
 
@@ -34,6 +34,7 @@ import numpy as np
 
 TENSOR_W, TENSOR_X, TENSOR_OUTLIERS, TENSOR_A, TENSOR_B, TENSOR_G, TENSOR_BIAS = 1, 2, 3, 4, 5, 6, 7
 TENSOR_W1, TENSOR_B1, TENSOR_W2, TENSOR_B2 = 8, 9, 10, 11   # bottleneck-MLP gate
+TENSOR_R = 12                                                # SERQ reconstruction matrix
 
 
 @dataclass(frozen=True)
@@ -133,6 +134,23 @@ def mlp_gate(spec: LayerSpec, rank: int, hidden: int, salt: int = 0):
     b2 = 1.0 + 0.5 * _rng(spec, TENSOR_B2, salt).standard_normal(rank)
     return {k: np.ascontiguousarray(v, dtype=np.float32)
             for k, v in (("w1", w1), ("b1", b1), ("w2", w2), ("b2", b2))}
+
+
+def serq_activations(spec: LayerSpec, tokens: int, salt: int = 0) -> np.ndarray:
+    """bf16 bits [tokens][d_in] for SERQ: the same draw as activations() with
+    the outlier channels at the front, [0, count) (SERQ's offline permutation
+    makes the salient channels contiguous), so salient_begin = 0."""
+    x = _rng(spec, TENSOR_X, salt).standard_normal((tokens, spec.d_in))
+    count = int(np.floor(spec.outlier_frac * spec.d_in + 0.5))
+    x[:, :count] *= spec.outlier_scale
+    return bf16_bits_from_f64(x)
+
+
+def serq_matrix(spec: LayerSpec, k: int, salt: int = 0) -> np.ndarray:
+    """SERQ's reconstruction matrix R, bf16 bits [d_out][k] ~ N(0, 0.01) (B's
+    distribution)."""
+    R = _rng(spec, TENSOR_R, salt).standard_normal((spec.d_out, k)) * 0.01
+    return np.ascontiguousarray(bf16_bits_from_f64(R))
 
 
 def small_spec(d_in: int, d_out: int, rank: int, group_size: int, asym: bool,

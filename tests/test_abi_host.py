@@ -110,6 +110,27 @@ def test_mlp_gate_validation_codes(lib):
     assert _call_mlp(lib, r0, 0, {}, 0) == binding.SPEAR_EC_OK
 
 
+def _call_serq(lib, desc, tokens, ptrs, s0, ws_bytes=1 << 30):
+    get = lambda k: ptrs.get(k)
+    return lib.spear_ec_linear_serq(ctypes.byref(desc) if desc is not None else None, tokens,
+                                    get("x"), get("wq"), get("sc"), get("z"), s0, get("B"),
+                                    get("y"), get("ws"), ws_bytes, None)
+
+
+def test_serq_validation_codes(lib):
+    good = q.make_desc(512, 512, 16, 512, False)
+    assert _call_serq(lib, good, 0, FAKE, 8) == binding.SPEAR_EC_OK
+    r0 = q.make_desc(512, 512, 0, 512, False)
+    assert _call_serq(lib, r0, 4, FAKE, 0) == binding.SPEAR_EC_ERR_UNSUPPORTED
+    for s0 in (-8, 4, 512 - 8, 512):  # negative, not a multiple of 8, past d_in
+        assert _call_serq(lib, good, 4, FAKE, s0) == binding.SPEAR_EC_ERR_INVALID_ARGUMENT
+    for k in ("B", "x", "y", "wq"):
+        assert _call_serq(lib, good, 4, {**FAKE, k: None}, 8) == binding.SPEAR_EC_ERR_INVALID_ARGUMENT
+    assert _call_serq(lib, good, 4, {**FAKE, "B": FAKE["B"] + 4}, 8) == binding.SPEAR_EC_ERR_MISALIGNED
+    assert _call_serq(lib, good, 4, FAKE, 8, ws_bytes=64) == binding.SPEAR_EC_ERR_WORKSPACE
+    assert _call_serq(lib, good, -1, FAKE, 8) == binding.SPEAR_EC_ERR_INVALID_ARGUMENT
+
+
 def test_decode_rejects_more_than_32_tokens(lib):
     d = q.make_desc(512, 512, 16, 512, False)
     assert _call(lib, "spear_ec_linear_decode", d, 33, FAKE, ws_bytes=1 << 40) == \

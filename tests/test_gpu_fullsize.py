@@ -108,8 +108,7 @@ class FullLayer:
 
 def test_full_size_mlp_gate_c3(torch):
     """The 70B down-projection with the bottleneck-MLP gate (h = 16): decode
-    with the correction workgroups (T = 16, 1) and prefill (T = 512), sampled
-    against the oracle."""
+    (T = 16, 1) and prefill (T = 512), sampled against the oracle."""
     L = FullLayer(torch, "c3")
     spec = L.spec
     m = synth.mlp_gate(spec, spec.rank, 16)
@@ -131,6 +130,31 @@ def test_full_size_mlp_gate_c3(torch):
                                       L.g, ti, ni, mlp=m)
         ok, st = check_sampled(from_dev_u16(y), ti, ni, yref)
         assert ok, (T, st)
+
+
+def test_full_size_serq_c3(torch):
+    """The 70B down-projection with SERQ's single-matrix reconstruction of 64
+    salient channels (at the front after the offline permutation, and at an
+    inner offset): decode (T = 16, 1, 32) and prefill (T = 512), sampled
+    against the oracle."""
+    L = FullLayer(torch, "c3")
+    spec = L.spec
+    k = 64
+    R = synth.serq_matrix(spec, k)
+    dR = to_dev_bf16(R)
+    desc = q.make_desc(L.K, L.N, k, L.g, L.asym)
+    for i, (T, s0) in enumerate(((16, 0), (1, 0), (32, 4096), (512, 0))):
+        x = synth.serq_activations(spec, T)
+        y = torch.empty((T, L.N), dtype=torch.bfloat16, device="cuda")
+        ws = q.alloc_workspace(desc, T)
+        note(f"  SERQ T={T} s0={s0}")
+        q.spear_ec_linear_serq(desc, to_dev_bf16(x), L.d_wq, L.d_sc, L.d_zs, s0, dR, y, ws)
+        torch.cuda.synchronize()
+        assert int(ws[:16].view(torch.int32)[3].item()) == 0
+        ti, ni = sample_points(T, L.N, 200, 800 + i)
+        yref = oracle.forward_serq_sampled(x, L.o_wq, L.o_sc, L.o_zs, s0, R, L.g, ti, ni)
+        ok, st = check_sampled(from_dev_u16(y), ti, ni, yref)
+        assert ok, (T, s0, st)
 
 
 @pytest.mark.parametrize("name,runs", [

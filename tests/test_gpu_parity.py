@@ -264,6 +264,37 @@ def test_mlp_gate_layer_matches_oracle(torch, K, N, r, h, g, asym, T):
         assert ok, (rep, st)
 
 
+SERQ_CASES = [
+    # K, N, k (salient channels), s0, g, asym, T
+    (1024, 400, 32, 0, 128, True, 1),
+    (1024, 400, 32, 64, 128, True, 16),
+    (1024, 400, 32, 984, 128, True, 33),     # last channels of x
+    (768, 272, 64, 8, 768, False, 24),
+    (768, 272, 64, 8, 768, False, 130),
+    (2048, 96, 128, 256, 128, False, 5),
+    (2048, 96, 128, 256, 128, False, 40),
+    (512, 48, 16, 496, 512, True, 32),
+]
+
+
+@pytest.mark.parametrize("K,N,k,s0,g,asym,T", SERQ_CASES)
+def test_serq_layer_matches_oracle(torch, K, N, k, s0, g, asym, T):
+    note(f"SERQ K={K} N={N} k={k} s0={s0} g={g} asym={asym} T={T}")
+    spec = synth.small_spec(K, N, k, g, asym, seed_base=12000 + K + T + s0)
+    L = Layer(torch, spec, T, x=synth.serq_activations(spec, T))
+    R = synth.serq_matrix(spec, k)
+    yref = oracle.forward_serq(L.x, L.o_wq, L.o_sc, L.o_zs, s0, R, L.g)
+    y = torch.empty((T, N), dtype=torch.bfloat16, device="cuda")
+    ws = q.alloc_workspace(L.desc, T)
+    for rep in range(2):   # the second call reuses the workspace
+        q.spear_ec_linear_serq(L.desc, to_dev_bf16(L.x), L.d_wq, L.d_sc, L.d_zs, s0,
+                               to_dev_bf16(R), y, ws)
+        torch.cuda.synchronize()
+        assert int(ws[:16].view(torch.int32)[3].item()) == 0
+        ok, st = check_bf16_output(from_dev_u16(y), yref)
+        assert ok, (rep, st)
+
+
 @pytest.mark.parametrize("K,N,r,g,asym", [(1024, 400, 32, 128, True), (512, 256, 16, 512, False)])
 def test_random_packed_bytes_through_both_paths(torch, K, N, r, g, asym):
     """Externally quantized weights (uniform random codes, scales and zero-points)."""

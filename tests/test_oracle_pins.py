@@ -469,3 +469,52 @@ def test_outputs_do_not_depend_on_batch_composition():
     for t in range(6):
         yt = _fwd(L, x=L["x"][t:t + 1])
         assert np.array_equal(yt[0], y[t])
+
+
+# SERQ single-matrix reconstruction (SERQ summary, section 2): y = W~ x + R x[S]
+# with S = [s0, s0 + k).
+
+def _serq_case(K, N, k, T, g, asym, seed):
+    L = _layer(K, N, k, T, g, asym, seed)
+    rng = np.random.default_rng(seed + 7000)
+    R = synth.bf16_bits_from_f64(rng.standard_normal((N, k)) * 0.05)
+    return L, R
+
+
+@pytest.mark.parametrize("s0", [0, 8, 40])
+def test_serq_is_spear_with_a_selector_and_a_unit_gate(s0):
+    # A = the 0/1 selector of channels s0 .. s0 + k, g = 0 and b = 1e30 (sigmoid
+    # exactly 1 in double), alpha = 1, B = R: the SPEAR forward then sums the
+    # same products in the same order, so the two agree bit for bit.
+    L, R = _serq_case(64, 40, 6, 3, 64, True, 31)
+    k, K = 6, 64
+    A = np.zeros((k, K), np.float64)
+    A[np.arange(k), s0 + np.arange(k)] = 1.0
+    y_serq = oracle.forward_serq(L["x"], L["wq"], L["sc"], L["zs"], s0, R, 64)
+    y_spear = oracle.forward(L["x"], L["wq"], L["sc"], L["zs"], synth.bf16_bits_from_f64(A), R,
+                             np.zeros(k, np.float32), np.full(k, 1e30, np.float32), 1.0, 64)
+    assert np.array_equal(y_serq, y_spear)
+
+
+def test_serq_with_zero_matrix_is_the_plain_w4_product():
+    L, R = _serq_case(64, 40, 6, 3, 64, False, 32)
+    y = oracle.forward_serq(L["x"], L["wq"], L["sc"], L["zs"], 16, np.zeros_like(R), 64)
+    assert np.array_equal(y, _fwd(L, alpha=0.0))
+
+
+@pytest.mark.parametrize("asym,g", [(False, 48), (True, 16)])
+def test_serq_matches_a_dense_matmul_with_the_scattered_matrix(asym, g):
+    # (W~ + R P) x with P the k x K selector, as one numpy matmul over the
+    # dequantized weights: a different summation path from the oracle's loops.
+    K, N, k, T, s0 = 48, 24, 5, 4, 16
+    L, R = _serq_case(K, N, k, T, g, asym, 33 + g)
+    Wt = oracle.dequant(L["wq"], L["sc"], L["zs"], K, g)
+    Rd = _bf(R)
+    Wfull = Wt.copy()
+    Wfull[:, s0:s0 + k] += Rd
+    y_ref = _xf(L) @ Wfull.T
+    y = oracle.forward_serq(L["x"], L["wq"], L["sc"], L["zs"], s0, R, g)
+    assert np.allclose(y, y_ref, rtol=1e-12, atol=1e-12)
+    ys = oracle.forward_serq_sampled(L["x"], L["wq"], L["sc"], L["zs"], s0, R, g,
+                                     [0, 3, 2], [0, 23, 7])
+    assert np.array_equal(ys, y[[0, 3, 2], [0, 23, 7]])
