@@ -204,6 +204,54 @@ int spear_ec_quantize_rtn(const spear_ec_desc* desc, const float* w, uint32_t* w
 int spear_ec_dequant_f32(const spear_ec_desc* desc, const uint32_t* wq, const void* scales,
                          const uint32_t* zeros, float* w_out, hipStream_t stream);
 
+/*
+ * EC-aware chunk selection (SPEAR summary, section 2.2 C: a latency-aware
+ * scheduler reads a precomputed table of kernel latencies and picks the
+ * largest prefill chunk that still meets the inter-token latency target, for
+ * the current compensator placement and decode load).  Host only.
+ *
+ * A step makes, per layer, one dispatcher call on the decode tokens and one
+ * on the prefill chunk.  Layers of one kind (shape and rank, e.g. with and
+ * without a compensator) share a table: us[i] is the latency of one call with
+ * tokens[i] tokens (ascending, >= 1), and `count` is how many calls of that
+ * kind one step makes per token group (its number of layers).  Between table
+ * points the latency is interpolated linearly over the table's running
+ * maximum; below the first point it is the first point's value, above the
+ * last it grows in proportion to the tokens; zero tokens cost nothing.
+ */
+typedef struct spear_ec_lut_kind {
+  int32_t n;              /* table points */
+  const int32_t* tokens;  /* [n], strictly ascending, >= 1 */
+  const float* us;        /* [n], finite, >= 0 */
+  int32_t count;          /* calls of this kind per token group in one step */
+} spear_ec_lut_kind;
+
+/* Latency (us) of a step with `decode_tokens` and a prefill chunk of
+ * `chunk_tokens`: overhead_us + sum_kinds count * (t(decode) + t(chunk)).
+ * Returns -1 for an invalid table or a negative token count. */
+float spear_ec_step_latency_us(const spear_ec_lut_kind* kinds, int32_t n_kinds,
+                               int32_t decode_tokens, int32_t chunk_tokens, float overhead_us);
+
+/* The largest multiple of `granule` up to `max_chunk` whose step latency is
+ * at most itl_us; 0 when even the decode tokens alone miss it (no prefill this
+ * step).  Returns -1 for an invalid table, decode_tokens < 0, max_chunk < 0,
+ * granule < 1 or a non-finite itl_us. */
+int32_t spear_ec_pick_chunk(const spear_ec_lut_kind* kinds, int32_t n_kinds, int32_t decode_tokens,
+                            float itl_us, float overhead_us, int32_t max_chunk, int32_t granule);
+
+/*
+ * Measure one kind's table on the device: for each of the n token counts,
+ * one untimed call of spear_ec_linear, then `reps` calls timed between two
+ * HIP events on `stream`, averaged into us_out[i].  x and y must hold
+ * max(tokens) rows; the other arguments are spear_ec_linear's.  Synchronizes
+ * the stream; creates and destroys two events.
+ */
+int spear_ec_lut_measure(const spear_ec_desc* desc, const int32_t* tokens, int32_t n, int32_t reps,
+                         const void* x, const uint32_t* wq, const void* scales,
+                         const uint32_t* zeros, const void* A, const void* B, const float* g,
+                         const float* b, float alpha, void* y, void* workspace,
+                         size_t workspace_bytes, hipStream_t stream, float* us_out);
+
 /* Static text for a status code. */
 const char* spear_ec_status_string(int status);
 

@@ -28,6 +28,7 @@ SPEAR_EC_DECODE_MAX_TOKENS = 32
 EXPORTED = (
     "spear_ec_workspace_bytes", "spear_ec_linear", "spear_ec_linear_decode",
     "spear_ec_linear_prefill", "spear_ec_linear_mlp_gate", "spear_ec_linear_serq",
+    "spear_ec_step_latency_us", "spear_ec_pick_chunk", "spear_ec_lut_measure",
     "spear_ec_quantize_rtn",
     "spear_ec_dequant_f32", "spear_ec_status_string", "spear_ec_last_error", "spear_ec_version",
 )
@@ -36,6 +37,11 @@ EXPORTED = (
 class spear_ec_desc(ctypes.Structure):
     _fields_ = [("d_in", ctypes.c_int32), ("d_out", ctypes.c_int32), ("rank", ctypes.c_int32),
                 ("group_size", ctypes.c_int32), ("flags", ctypes.c_int32)]
+
+
+class spear_ec_lut_kind(ctypes.Structure):
+    _fields_ = [("n", ctypes.c_int32), ("tokens", ctypes.POINTER(ctypes.c_int32)),
+                ("us", ctypes.POINTER(ctypes.c_float)), ("count", ctypes.c_int32)]
 
 
 class SpearEcError(RuntimeError):
@@ -69,6 +75,15 @@ def load_library(path: str = LIB_PATH):
     lib.spear_ec_linear_mlp_gate.restype = ctypes.c_int
     lib.spear_ec_linear_serq.argtypes = [DP, i32, P, P, P, P, i32, P, P, P, sz, P]
     lib.spear_ec_linear_serq.restype = ctypes.c_int
+    KP = ctypes.POINTER(spear_ec_lut_kind)
+    f32 = ctypes.c_float
+    lib.spear_ec_step_latency_us.argtypes = [KP, i32, i32, i32, f32]
+    lib.spear_ec_step_latency_us.restype = f32
+    lib.spear_ec_pick_chunk.argtypes = [KP, i32, i32, f32, f32, i32, i32]
+    lib.spear_ec_pick_chunk.restype = i32
+    lib.spear_ec_lut_measure.argtypes = [DP, ctypes.POINTER(i32), i32, i32, P, P, P, P, P, P, P, P,
+                                         f32, P, P, sz, P, ctypes.POINTER(f32)]
+    lib.spear_ec_lut_measure.restype = ctypes.c_int
     lib.spear_ec_quantize_rtn.argtypes = [DP, P, P, P, P, P]
     lib.spear_ec_quantize_rtn.restype = ctypes.c_int
     lib.spear_ec_dequant_f32.argtypes = [DP, P, P, P, P, P]
@@ -177,6 +192,47 @@ def spear_ec_linear_serq(desc, x, wq, scales, zeros, salient_begin, R, y, worksp
     _check(load_library().spear_ec_linear_serq(
         ctypes.byref(desc), tokens, _ptr(x), _ptr(wq), _ptr(scales), _ptr(zeros),
         int(salient_begin), _ptr(R), _ptr(y), _ptr(workspace), ws_bytes, _stream(stream)))
+
+
+def _kinds(kinds):
+    """[{tokens, us, count}] -> a ctypes array of spear_ec_lut_kind (and the
+    arrays it points to, kept alive with it)."""
+    keep = []
+    arr = (spear_ec_lut_kind * max(1, len(kinds)))()
+    for i, k in enumerate(kinds):
+        t = (ctypes.c_int32 * len(k["tokens"]))(*[int(v) for v in k["tokens"]])
+        u = (ctypes.c_float * len(k["us"]))(*[float(v) for v in k["us"]])
+        keep += [t, u]
+        arr[i] = spear_ec_lut_kind(len(k["tokens"]), t, u, int(k["count"]))
+    return arr, keep
+
+
+def spear_ec_step_latency_us(kinds, decode_tokens, chunk_tokens, overhead_us=0.0) -> float:
+    arr, _keep = _kinds(kinds)
+    return float(load_library().spear_ec_step_latency_us(arr, len(kinds), int(decode_tokens),
+                                                         int(chunk_tokens), float(overhead_us)))
+
+
+def spear_ec_pick_chunk(kinds, decode_tokens, itl_us, overhead_us=0.0, max_chunk=8192,
+                        granule=32) -> int:
+    arr, _keep = _kinds(kinds)
+    return int(load_library().spear_ec_pick_chunk(arr, len(kinds), int(decode_tokens),
+                                                  float(itl_us), float(overhead_us),
+                                                  int(max_chunk), int(granule)))
+
+
+def spear_ec_lut_measure(desc, tokens, reps, x, wq, scales, zeros, A, B, g, b, alpha, y,
+                         workspace, stream=None):
+    """Latency (us) of one spear_ec_linear call at each token count."""
+    n = len(tokens)
+    t = (ctypes.c_int32 * n)(*[int(v) for v in tokens])
+    out = (ctypes.c_float * n)()
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check(load_library().spear_ec_lut_measure(
+        ctypes.byref(desc), t, n, int(reps), _ptr(x), _ptr(wq), _ptr(scales), _ptr(zeros), _ptr(A),
+        _ptr(B), _ptr(g), _ptr(b), float(alpha), _ptr(y), _ptr(workspace), ws_bytes,
+        _stream(stream), out))
+    return [float(v) for v in out]
 
 
 def spear_ec_quantize_rtn(desc, w, wq, scales, zeros, stream=None):

@@ -368,6 +368,38 @@ int spear_ec_linear_serq(const spear_ec_desc* desc, int32_t tokens, const void* 
                      workspace_bytes, stream);
 }
 
+int spear_ec_lut_measure(const spear_ec_desc* desc, const int32_t* tokens, int32_t n, int32_t reps,
+                         const void* x, const uint32_t* wq, const void* scales,
+                         const uint32_t* zeros, const void* A, const void* B, const float* g,
+                         const float* b, float alpha, void* y, void* workspace,
+                         size_t workspace_bytes, hipStream_t stream, float* us_out) {
+  g_last_error[0] = 0;
+  if (!tokens || !us_out || n < 1 || reps < 1)
+    return fail(SPEAR_EC_ERR_INVALID_ARGUMENT, "tokens, us_out, n >= 1 and reps >= 1 are required");
+  for (int32_t i = 0; i < n; ++i)
+    if (tokens[i] < 1 || (i > 0 && tokens[i] <= tokens[i - 1]))
+      return fail(SPEAR_EC_ERR_INVALID_ARGUMENT, "tokens must be >= 1 and strictly ascending");
+  hipEvent_t e0 = nullptr, e1 = nullptr;
+  int rc = hip_status(hipEventCreate(&e0), "event create");
+  if (!rc) rc = hip_status(hipEventCreate(&e1), "event create");
+  for (int32_t i = 0; i < n && !rc; ++i) {
+    rc = linear(kAuto, desc, tokens[i], x, wq, scales, zeros, A, B, g, b, alpha, y, workspace,
+                workspace_bytes, stream);
+    if (!rc) rc = hip_status(hipEventRecord(e0, stream), "event record");
+    for (int32_t k = 0; k < reps && !rc; ++k)
+      rc = linear(kAuto, desc, tokens[i], x, wq, scales, zeros, A, B, g, b, alpha, y, workspace,
+                  workspace_bytes, stream);
+    if (!rc) rc = hip_status(hipEventRecord(e1, stream), "event record");
+    if (!rc) rc = hip_status(hipEventSynchronize(e1), "event synchronize");
+    float ms = 0.f;
+    if (!rc) rc = hip_status(hipEventElapsedTime(&ms, e0, e1), "event elapsed time");
+    if (!rc) us_out[i] = ms * 1000.f / (float)reps;
+  }
+  if (e0) (void)hipEventDestroy(e0);
+  if (e1) (void)hipEventDestroy(e1);
+  return rc;
+}
+
 int spear_ec_quantize_rtn(const spear_ec_desc* desc, const float* w, uint32_t* wq, void* scales,
                           uint32_t* zeros, hipStream_t stream) {
   g_last_error[0] = 0;

@@ -1,0 +1,138 @@
+"""EC-aware chunk selection from a latency table (SPEAR summary, section 2.2 C).
+
+The oracle (oracle/scheduler.py, plain loops over every candidate chunk) is
+pinned to hand-worked values; the library's selection (host C++, bisection)
+must equal it exactly on seeded synthetic tables.  One GPU test measures a
+real table through the library and checks the selection against it.
+"""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+
+from oracle import scheduler as ref
+import quantization_error_compensation_amd as q
+
+
+
+def _hand(golden):
+    return golden["chunk_schedule"]
+
+
+def test_oracle_hand_examples(golden):
+    h = _hand(golden)
+    kinds = h["kinds"]
+    assert ref.step_us(kinds, 16, 256) == h["step_16_256"]
+    assert ref.pick_chunk(kinds, 16, 16000.0, 0.0, 8192, 32) == h["pick_16_16000_g32"]
+    assert ref.pick_chunk(kinds, 16, 1999.0, 0.0, 8192, 32) == h["pick_16_1999_g32"]
+    assert ref.step_us(kinds, 0, 600) == h["step_0_600"]
+
+
+def test_oracle_properties():
+    kinds = [{"tokens": [1, 8, 64], "us": [10.0, 9.0, 40.0], "count": 2}]
+    # the running maximum: 8 tokens cost what 1 does (9 < 10 is raised to 10)
+    assert ref.call_us(kinds[0]["tokens"], kinds[0]["us"], 8) == 10.0
+    assert ref.call_us(kinds[0]["tokens"], kinds[0]["us"], 0) == 0.0
+    # below the first point: the first point's latency
+    assert ref.call_us([4, 8], [5.0, 6.0], 1) == 5.0
+    # non-decreasing in the chunk
+    s = [ref.step_us(kinds, 3, c) for c in range(0, 300)]
+    assert all(b >= a for a, b in zip(s, s[1:]))
+    # a bigger budget never picks a smaller chunk
+    p = [ref.pick_chunk(kinds, 3, itl, 0.0, 512, 16) for itl in np.linspace(0, 400, 41)]
+    assert all(b >= a for a, b in zip(p, p[1:]))
+
+
+def test_library_matches_hand_examples(golden):
+    h = _hand(golden)
+    kinds = h["kinds"]
+    assert q.spear_ec_step_latency_us(kinds, 16, 256) == pytest.approx(h["step_16_256"], rel=1e-6)
+    assert q.spear_ec_pick_chunk(kinds, 16, 16000.0, 0.0, 8192, 32) == h["pick_16_16000_g32"]
+    assert q.spear_ec_pick_chunk(kinds, 16, 1999.0, 0.0, 8192, 32) == h["pick_16_1999_g32"]
+
+
+def _random_kinds(rng):
+    kinds = []
+    for _ in range(rng.integers(1, 4)):
+        n = int(rng.integers(1, 7))
+        toks = np.sort(rng.choice(np.arange(1, 4097), size=n, replace=False))
+        us = np.cumsum(rng.uniform(0.0, 60.0, n)) + rng.uniform(5, 20)
+        if rng.random() < 0.3:  # noisy, non-monotone measurements
+            us = us * rng.uniform(0.8, 1.2, n)
+        kinds.append({"tokens": [int(t) for t in toks],
+                      "us": [float(np.float32(u)) for u in us],
+                      "count": int(rng.integers(0, 100))})
+    return kinds
+
+
+def test_library_matches_oracle_on_random_tables():
+    rng = np.random.default_rng(2024)
+    for case in range(300):
+        kinds = _random_kinds(rng)
+        d = int(rng.integers(0, 64))
+        over = float(np.float32(rng.uniform(0, 500)))
+        gran = int(rng.choice([1, 16, 32, 64]))
+        mx = int(rng.integers(0, 4096))
+        # budgets around the interesting range, as fp32 values (the C side's type)
+        lo, hi = ref.step_us(kinds, d, 0, over), ref.step_us(kinds, d, mx, over)
+        itl = float(np.float32(rng.uniform(lo * 0.9, hi * 1.1 + 1)))
+        got = q.spear_ec_pick_chunk(kinds, d, itl, over, mx, gran)
+        want = ref.pick_chunk(kinds, d, itl, over, mx, gran)
+        if got != want:  # allowed only where fp rounding decides a tie at the budget
+            s_got = ref.step_us(kinds, d, got, over)
+            s_next = ref.step_us(kinds, d, want, over)
+            assert abs(s_got - itl) < 1e-9 * max(1, itl) or abs(s_next - itl) < 1e-9 * max(1, itl), \
+                (case, got, want)
+        c = int(rng.integers(0, 5000))
+        assert q.spear_ec_step_latency_us(kinds, d, c, over) == \
+            pytest.approx(ref.step_us(kinds, d, c, over), rel=1e-6)
+
+
+def test_library_edge_cases():
+    k = [{"tokens": [1, 32, 256], "us": [10.0, 20.0, 100.0], "count": 4}]
+    assert q.spear_ec_pick_chunk(k, 8, 1e9, 0.0, 1000, 64) == 960        # all of max_chunk
+    assert q.spear_ec_pick_chunk(k, 8, 1e9, 0.0, 0, 64) == 0
+    assert q.spear_ec_pick_chunk([], 8, 5.0, 1.0, 512, 32) == 512         # no layers: overhead only
+    assert q.spear_ec_pick_chunk([], 8, 0.5, 1.0, 512, 32) == 0
+    # invalid tables and arguments
+    bad = [
+        [{"tokens": [4, 4], "us": [1.0, 2.0], "count": 1}],     # not strictly ascending
+        [{"tokens": [0, 4], "us": [1.0, 2.0], "count": 1}],     # tokens < 1
+        [{"tokens": [1, 4], "us": [1.0, -2.0], "count": 1}],    # negative latency
+        [{"tokens": [1, 4], "us": [1.0, float("nan")], "count": 1}],
+        [{"tokens": [1], "us": [1.0], "count": -1}],
+    ]
+    for kinds in bad:
+        assert q.spear_ec_pick_chunk(kinds, 1, 100.0, 0.0, 64, 16) == -1
+        assert q.spear_ec_step_latency_us(kinds, 1, 1, 0.0) == -1.0
+    assert q.spear_ec_pick_chunk(k, -1, 100.0, 0.0, 64, 16) == -1
+    assert q.spear_ec_pick_chunk(k, 1, 100.0, 0.0, 64, 0) == -1
+    assert q.spear_ec_pick_chunk(k, 1, float("inf"), 0.0, 64, 16) == -1
+
+
+@pytest.mark.gpu
+def test_measured_table_drives_the_selection():
+    import torch
+    import synth
+    from helpers import to_dev_bf16, to_dev_f32
+    spec = synth.CONFIGS["c1"]
+    K, N, g, asym, r = spec.d_in, spec.d_out, spec.group_size, spec.asym, spec.rank
+    tokens = [1, 16, 32, 64, 128, 256]
+    print(f"lut measure c1 tokens={tokens}", flush=True)
+    desc = q.make_desc(K, N, r, g, asym)
+    wq, sc, zs = q.alloc_packed(desc)
+    q.spear_ec_quantize_rtn(desc, to_dev_f32(synth.weights(spec)), wq, sc, zs)
+    A, B, gv, bv = synth.compensator(spec)
+    x = to_dev_bf16(synth.activations(spec, max(tokens)))
+    y = torch.empty((max(tokens), N), dtype=torch.bfloat16, device="cuda")
+    ws = q.alloc_workspace(desc, max(tokens))
+    us = q.spear_ec_lut_measure(desc, tokens, 5, x, wq, sc, zs, to_dev_bf16(A), to_dev_bf16(B),
+                                to_dev_f32(gv), to_dev_f32(bv), 1.0, y, ws)
+    assert all(np.isfinite(us)) and all(u > 0 for u in us), us
+    kinds = [{"tokens": tokens, "us": us, "count": 32}]
+    budget = q.spear_ec_step_latency_us(kinds, 16, 128, 50.0)
+    c = q.spear_ec_pick_chunk(kinds, 16, budget, 50.0, 1024, 32)
+    assert 128 <= c <= 1024
+    assert c == ref.pick_chunk(kinds, 16, budget, 50.0, 1024, 32) or \
+        abs(ref.step_us(kinds, 16, c, 50.0) - budget) < 1e-3
+    assert q.spear_ec_step_latency_us(kinds, 16, c, 50.0) <= budget
