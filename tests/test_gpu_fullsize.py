@@ -5,7 +5,8 @@ Each workload's layer is built at its real shape, quantized by both sides
 bench.py calls it (one workspace sized for the call's token count).  The fp64
 oracle is too slow for every output of these layers, so it computes a sample
 of outputs one by one: the first and last token, the first and last rows,
-rows on both sides of every 64-row band edge that the sample draws, and
+rows on both sides of the 128-row band edges (decode bands; every other one
+is a 256-row prefill tile edge) that the sample draws, and
 random (token, row) pairs.  The sampled outputs meet the same elementwise bar
 as the small cases; every output must be finite.
 """
@@ -39,7 +40,7 @@ def sample_points(T, N, n_random, seed):
     rng = np.random.default_rng(seed)
     ts = [0, T - 1] + list(rng.integers(0, T, n_random))
     ns = [0, N - 1] + list(rng.integers(0, N, n_random))
-    edges = rng.integers(1, max(2, N // 64), 4) * 64          # band edges: rows 64k - 1, 64k
+    edges = rng.integers(1, max(2, N // 128), 4) * 128        # band edges: rows 128k - 1, 128k
     for e in edges:
         if e < N:
             ts += [int(rng.integers(0, T)), int(rng.integers(0, T))]
