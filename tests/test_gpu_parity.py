@@ -167,6 +167,13 @@ LAYER_CASES = [
     (2048, 96, 128, 128, False, 77),
     (640, 160, 0, 640, True, 9),        # rank 0: plain W4, asymmetric per-channel
     (640, 160, 0, 640, True, 150),
+    # odd block counts per row (9, 3): decode runs that start on an odd block
+    # move one unit on, runs cross band edges, r = 48 repeats a rank tile
+    (1152, 400, 48, 128, True, 7),
+    (1152, 400, 48, 128, True, 24),
+    (1152, 400, 48, 128, True, 40),
+    (384, 208, 16, 384, False, 3),
+    (384, 208, 16, 384, False, 31),
 ]
 
 
