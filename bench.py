@@ -103,6 +103,9 @@ def parse():
                     help="SERQ single-matrix reconstruction of K salient channels (the first K "
                          "after the permutation) instead of the SPEAR compensator")
     ap.add_argument("--copies", type=int, default=0, help="weight copies to rotate (0 = auto)")
+    ap.add_argument("--sweep", action="store_true",
+                    help="rank sweep: run the config's calls at every rank of the nested "
+                         "compensator draws (0, 16, 64, 128) and report t(r)/t(0) - 1 per call")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run one plain device copy of known size (for HBM counter scaling)")
@@ -123,6 +126,9 @@ def main():
         print("bench.py measures one GPU only: this build has no multi-GPU path "
               "(run with --gpus 1).", file=sys.stderr)
         sys.exit(2)
+    if args.sweep:
+        rank_sweep(args)
+        return
 
     import torch
 
@@ -214,16 +220,18 @@ def main():
     torch.cuda.synchronize()
     ms_total = start.elapsed_time(end)
     ms_step = ms_total / args.steps
-    per_call_ms = [float(np.mean([evs[i][j].elapsed_time(evs[i][j + 1]) for i in range(args.steps)]))
-                   for j in range(n)]
+    call_ms = [np.array([evs[i][j].elapsed_time(evs[i][j + 1]) for i in range(args.steps)])
+               for j in range(n)]
+    per_call_ms = [float(np.mean(v)) for v in call_ms]
 
     calls = []
     for j, (path, T) in enumerate(plan):
         by = layer_bytes(K, N, r, g, asym, T, serq)
         fl = layer_flops(K, N, r, T, serq)
         s = per_call_ms[j] / 1e3
-        calls.append(dict(path=path, tokens=T, ms=per_call_ms[j], bytes=by, flops=fl,
-                          gbs=by / s / 1e9, tflops=fl / s / 1e12))
+        p10, p50, p90 = (float(v) for v in np.percentile(call_ms[j], [10, 50, 90]))
+        calls.append(dict(path=path, tokens=T, ms=per_call_ms[j], p10_ms=p10, p50_ms=p50,
+                          p90_ms=p90, bytes=by, flops=fl, gbs=by / s / 1e9, tflops=fl / s / 1e12))
 
     if args.copy_calibration:
         a = torch.empty(1 << 28, dtype=torch.uint8, device=dev)   # 256 MiB
@@ -280,6 +288,43 @@ def main():
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(spec, r, plan, X, A, B, gv, bv, unit, mlp, serq)
     print(json.dumps(out), flush=True)
+
+
+def rank_sweep(args):
+    """Each rank of the nested draws in a child process of its own (this
+    process never touches the GPU); per call, the time relative to rank 0 and
+    the compensator's bytes relative to the W4 layer's, 2r(K+N) / (KN/2 +
+    scales + zeros)."""
+    import subprocess
+
+    import synth
+    spec = synth.CONFIGS[args.config]
+    K, N, g, asym = spec.d_in, spec.d_out, spec.group_size, spec.asym
+    runs = {}
+    for r in (0, 16, 64, 128):
+        cmd = [sys.executable, os.path.abspath(__file__), "--config", args.config, "--rank", str(r),
+               "--steps", str(args.steps), "--warmup", str(args.warmup), "--no-cpu-baseline"]
+        if args.copies:
+            cmd += ["--copies", str(args.copies)]
+        res = subprocess.run(cmd, capture_output=True, text=True)
+        if res.returncode:
+            sys.stderr.write(res.stderr)
+            sys.exit(res.returncode)
+        runs[r] = json.loads(res.stdout.strip().splitlines()[-1])
+        print(f"rank {r}: " + ", ".join(f"{c['path']} T={c['tokens']} {c['ms'] * 1e3:.2f} us"
+                                        for c in runs[r]["calls"]), file=sys.stderr, flush=True)
+    w4 = weight_bytes(K, N, 0, g, asym)
+    table = []
+    for r, run in runs.items():
+        for c, c0 in zip(run["calls"], runs[0]["calls"]):
+            table.append({"rank": r, "path": c["path"], "tokens": c["tokens"],
+                          "us": round(c["ms"] * 1e3, 2), "p50_us": round(c["p50_ms"] * 1e3, 2),
+                          "rel_to_rank0": round(c["ms"] / c0["ms"] - 1.0, 4),
+                          "ec_bytes_over_w4": round(2 * r * (K + N) / w4, 4)})
+    print(json.dumps({"metric": "rank sweep: call time relative to rank 0 (t(r)/t(0) - 1)",
+                      "config": args.config, "steps": args.steps, "warmup": args.warmup,
+                      "weight_copies_rotated": runs[0]["config"]["weight_copies_rotated"],
+                      "kernel_source_hash": kernel_source_hash(), "sweep": table}), flush=True)
 
 
 CALIB_BYTES = 1 << 28   # the --copy-calibration copy: 256 MiB read, 256 MiB written
