@@ -232,9 +232,9 @@ typedef struct spear_ec_lut_kind {
 float spear_ec_step_latency_us(const spear_ec_lut_kind* kinds, int32_t n_kinds,
                                int32_t decode_tokens, int32_t chunk_tokens, float overhead_us);
 
-/* The largest multiple of `granule` up to `max_chunk` whose step latency is
- * at most itl_us; 0 when even the decode tokens alone miss it (no prefill this
- * step).  Returns -1 for an invalid table, decode_tokens < 0, max_chunk < 0,
+/* The largest multiple of `granule` up to `max_chunk` whose step latency, as
+ * spear_ec_step_latency_us returns it (fp32), is at most itl_us; 0 when even
+ * the decode tokens alone miss it (no prefill this step).  Returns -1 for an invalid table, decode_tokens < 0, max_chunk < 0,
  * granule < 1 or a non-finite itl_us. */
 int32_t spear_ec_pick_chunk(const spear_ec_lut_kind* kinds, int32_t n_kinds, int32_t decode_tokens,
                             float itl_us, float overhead_us, int32_t max_chunk, int32_t granule);

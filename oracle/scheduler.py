@@ -13,12 +13,17 @@ latency target.  The readings (the pages give no formula):
     first point it is the first point's latency; above the last it is the
     last latency scaled by tokens / last tokens; zero tokens cost nothing;
   * the chosen chunk is a multiple of a granule up to a maximum; when even
-    the decode tokens alone exceed the target the chunk is 0.
+    the decode tokens alone exceed the target the chunk is 0;
+  * a step meets the target when its latency, rounded to fp32 (the precision
+    a latency is reported in), is at most the fp32 target, so a latency read
+    back from the table selects the chunk it was computed for.
 
 Written with plain loops over every candidate chunk (no bisection), in Python
-floats (double).
+floats (double), with the one fp32 rounding of the comparison.
 """
 from __future__ import annotations
+
+import numpy as np
 
 
 def call_us(tokens, us, t):
@@ -50,6 +55,6 @@ def pick_chunk(kinds, decode_tokens, itl_us, overhead_us=0.0, max_chunk=8192, gr
     best = 0
     for m in range(0, max_chunk // granule + 1):
         c = m * granule
-        if step_us(kinds, decode_tokens, c, overhead_us) <= itl_us:
+        if np.float32(step_us(kinds, decode_tokens, c, overhead_us)) <= np.float32(itl_us):
             best = c
     return best

@@ -80,8 +80,10 @@ int32_t spear_ec_pick_chunk(const spear_ec_lut_kind* kinds, int32_t n_kinds, int
   // The step latency never decreases with the chunk, so the largest chunk
   // meeting the target is found by bisection over the multiples of granule.
   const int32_t hi_n = max_chunk / granule;
+  // Compared in fp32, the precision spear_ec_step_latency_us reports: a
+  // latency read back from it selects the chunk it was computed for.
   auto fits = [&](int32_t m) {
-    return step_us(kinds, n_kinds, decode_tokens, m * granule, overhead_us) <= (double)itl_us;
+    return (float)step_us(kinds, n_kinds, decode_tokens, m * granule, overhead_us) <= itl_us;
   };
   if (!fits(0)) return 0;  // not even the decode tokens alone: no prefill this step
   int32_t lo = 0, hi = hi_n;

@@ -110,6 +110,22 @@ def test_library_edge_cases():
     assert q.spear_ec_pick_chunk(k, 1, float("inf"), 0.0, 64, 16) == -1
 
 
+def test_reported_latency_selects_its_own_chunk():
+    """A target equal to the (fp32) latency the library reports for a chunk
+    selects that chunk, also when the exact latency rounds down to fp32."""
+    found = False
+    for count in range(1, 200):
+        kinds = [{"tokens": [1, 256], "us": [1.0, 3.0], "count": count}]
+        exact = ref.step_us(kinds, 16, 128, 50.0)
+        budget = q.spear_ec_step_latency_us(kinds, 16, 128, 50.0)
+        assert budget == np.float32(exact)
+        if float(budget) < exact:  # rounded down: the exact latency misses the target
+            found = True
+            assert q.spear_ec_pick_chunk(kinds, 16, budget, 50.0, 1024, 32) == 128
+            assert ref.pick_chunk(kinds, 16, budget, 50.0, 1024, 32) == 128
+    assert found
+
+
 @pytest.mark.gpu
 def test_measured_table_drives_the_selection():
     import torch
