@@ -69,7 +69,8 @@ def test_graph_replay_matches_eager(torch, K, N, r, g, asym, Td, Tp):
     o_wq, o_sc, o_zs = oracle.quantize_rtn(W, g, asym)
     for bits, out in ((xd_bits, ref_d), (xp_bits, ref_p)):
         y_ref = oracle.forward(bits, o_wq, o_sc, o_zs, A if r else None, B, gv, bv, spec.alpha, g)
-        check_bf16_output(out, y_ref)
+        ok, st = check_bf16_output(out, y_ref)
+        assert ok, st
 
     cap = torch.cuda.Stream()
     graph = torch.cuda.CUDAGraph()

@@ -400,6 +400,40 @@ def test_mlp_gate_factored_path_equals_explicit_effective_weight(h):
     assert not np.allclose(y, yc, rtol=1e-6, atol=1e-9)
 
 
+@pytest.mark.parametrize("r,h", [(6, 3), (5, 9), (8, 1)])
+def test_mlp_gate_matches_an_independent_numpy_evaluation(r, h):
+    # gamma(u) = sigmoid(W2 relu(W1 u + b1) + b2) evaluated by numpy matrix
+    # products and scipy's logistic function over the header's layouts
+    # (w1 [h][r], w2 [r][h]) with h != r and non-symmetric random weights, so
+    # a transposed W1 or W2 (or a swapped bias) gives other numbers.  u comes
+    # from the oracle and is itself pinned to x A^T by numpy.
+    L = _layer(64, 24, r, 4, 16, True, 40 + r + h)
+    rng = np.random.default_rng(900 + 10 * r + h)
+    m = {"w1": rng.standard_normal((h, r)).astype(np.float32),
+         "b1": (0.3 * rng.standard_normal(h)).astype(np.float32),
+         "w2": rng.standard_normal((r, h)).astype(np.float32),
+         "b2": (0.5 * rng.standard_normal(r)).astype(np.float32)}
+    y, u, v = oracle.forward(L["x"], L["wq"], L["sc"], L["zs"], L["A"], L["B"], None, None, 0.8,
+                             16, return_uv=True, mlp=m)
+    uref = _xf(L) @ _bf(L["A"]).T
+    assert np.allclose(u, uref, rtol=1e-14, atol=1e-14)
+    w1, b1 = m["w1"].astype(np.float64), m["b1"].astype(np.float64)
+    w2, b2 = m["w2"].astype(np.float64), m["b2"].astype(np.float64)
+    hid = np.maximum(uref @ w1.T + b1, 0.0)                  # [T][h]
+    gam = expit(hid @ w2.T + b2)                              # [T][r]
+    assert np.any((hid > 0) & (hid < 1e3)) and np.any(hid == 0.0)   # relu active both ways
+    assert np.allclose(v, gam * uref, rtol=1e-12, atol=1e-14)
+    Wt = oracle.dequant(L["wq"], L["sc"], L["zs"], 64, 16)
+    a32 = float(np.float32(0.8))                              # alpha crosses the ABI as fp32
+    yref = _xf(L) @ Wt.T + a32 * (gam * uref) @ _bf(L["B"]).T
+    assert np.allclose(y, yref, rtol=1e-12, atol=1e-13)
+    # the sampled form uses the same gate
+    ti, ni = np.array([0, 3, 1, 2]), np.array([23, 0, 7, 11])
+    ys = oracle.forward_sampled(L["x"], L["wq"], L["sc"], L["zs"], L["A"], L["B"], None, None,
+                                0.8, 16, ti, ni, mlp=m)
+    assert np.array_equal(ys, y[ti, ni])
+
+
 def test_correction_vanishes_when_projection_is_zero():
     L = _layer(64, 40, 6, 4, 64, False, 13)
     A = _bf(L["A"]).copy()
@@ -461,6 +495,26 @@ def test_sampled_forward_matches_full_forward():
     ys = oracle.forward_sampled(L["x"], L["wq"], L["sc"], L["zs"], L["A"], L["B"], L["g"],
                                 L["b"], 1.0, 32, ti, ni)
     assert np.array_equal(ys, y[ti, ni])
+
+
+@pytest.mark.parametrize("alpha", [0.0, 0.7, -1.3])
+def test_sampled_forward_matches_full_forward_at_any_alpha(alpha):
+    # forward_sampled is the reference of the full-size GPU checks; at
+    # alpha != 1 it must scale the correction exactly as the full forward
+    # does, and at alpha = 0 give the plain W4 product of numpy.
+    L = _layer(128, 40, 8, 4, 32, True, 60)
+    y = _fwd(L, alpha=alpha)
+    rng = np.random.default_rng(61)
+    ti = rng.integers(0, 4, 30)
+    ni = rng.integers(0, 40, 30)
+    ys = oracle.forward_sampled(L["x"], L["wq"], L["sc"], L["zs"], L["A"], L["B"], L["g"],
+                                L["b"], alpha, 32, ti, ni)
+    assert np.array_equal(ys, y[ti, ni])
+    Wt = oracle.dequant(L["wq"], L["sc"], L["zs"], 128, 32)
+    u = _xf(L) @ _bf(L["A"]).T
+    v = expit(L["g"].astype(np.float64) * u + L["b"].astype(np.float64)) * u
+    yref = _xf(L) @ Wt.T + float(np.float32(alpha)) * v @ _bf(L["B"]).T   # alpha is fp32
+    assert np.allclose(ys, yref[ti, ni], rtol=1e-12, atol=1e-13)
 
 
 def test_outputs_do_not_depend_on_batch_composition():
