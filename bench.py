@@ -12,9 +12,19 @@ rotate over several copies so no call finds them in the 256 MB last-level
 cache from an earlier step.  Inputs are seeded synthetic tensors of the
 workload's shapes and distributions, resident in HBM before timing starts.
 
+Timing.  The K timed steps run back to back between two events
+(ms_per_step).  Then each call of the step is timed on its own: the same
+call launched K times back to back between two events on the launch stream,
+rotating the weight copies (its mean duration: the kernel time plus the
+launch gap, what a kernel trace of the same run averages), and once more with
+an event pair around every launch (p10/p50/p90; these include the events' own
+overhead of a few microseconds).  Each timed batch is queued behind a spin
+kernel long enough for the host to enqueue the whole batch first, so the
+host's launch overhead never leaves the GPU idle inside a timed interval.
+
 Reported (one JSON line):
   value        decode effective bandwidth: algorithmic bytes of the decode
-               call / its duration (GB/s); prefill TFLOP/s alongside.
+               call / its mean duration (GB/s); prefill TFLOP/s alongside.
   roofline     for the dominant call (prefill, matrix cores) and, under
                roofline_decode, for the decode call (HBM).
   cpu_baseline the single-threaded fp64 oracle on a row slice of the same
@@ -185,44 +195,87 @@ def main():
 
     stream = torch.cuda.current_stream()
 
-    def step(i, evs=None):
+    def call(j, i):
+        """Call j of the step on weight copy i (mod copies)."""
         L = layers[i % copies]
-        for j, (path, T) in enumerate(plan):
-            if evs is not None:
-                evs[j].record(stream)
-            if serq:
-                q.spear_ec_linear_serq(desc, xs[j], L["wq"], L["sc"], L["zs"], 0, L["B"], ys[j],
-                                       ws, stream)
-            elif L["mlp"] is not None:
-                m = L["mlp"]
-                q.spear_ec_linear_mlp_gate(desc, xs[j], L["wq"], L["sc"], L["zs"], L["A"], L["B"],
-                                           m["w1"], m["b1"], m["w2"], m["b2"], spec.alpha, ys[j],
-                                           ws, stream)
-            else:
-                q.spear_ec_linear(desc, xs[j], L["wq"], L["sc"], L["zs"], L["A"], L["B"],
-                                  L["g"], L["b"], spec.alpha, ys[j], ws, stream)
-        if evs is not None:
-            evs[len(plan)].record(stream)
+        if serq:
+            q.spear_ec_linear_serq(desc, xs[j], L["wq"], L["sc"], L["zs"], 0, L["B"], ys[j], ws,
+                                   stream)
+        elif L["mlp"] is not None:
+            m = L["mlp"]
+            q.spear_ec_linear_mlp_gate(desc, xs[j], L["wq"], L["sc"], L["zs"], L["A"], L["B"],
+                                       m["w1"], m["b1"], m["w2"], m["b2"], spec.alpha, ys[j], ws,
+                                       stream)
+        else:
+            q.spear_ec_linear(desc, xs[j], L["wq"], L["sc"], L["zs"], L["A"], L["B"], L["g"],
+                              L["b"], spec.alpha, ys[j], ws, stream)
+
+    def step(i):
+        for j in range(len(plan)):
+            call(j, i)
 
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
 
     n = len(plan)
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(n + 1)] for _ in range(args.steps)]
+    # host enqueue time per call, and the spin kernel's rate, to size the
+    # spin that holds the GPU while a timed batch is enqueued
+    torch.cuda.synchronize()
+    h0 = time.perf_counter()
+    for i in range(args.warmup):
+        step(i)
+    host_s = (time.perf_counter() - h0) / max(1, args.warmup * n)
+    torch.cuda.synchronize()
+    c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    c0.record(stream)
+    torch.cuda._sleep(1 << 22)
+    c1.record(stream)
+    torch.cuda.synchronize()
+    spin_s_per_cycle = c0.elapsed_time(c1) / 1e3 / (1 << 22)
+
+    def hold(launches):
+        """Keep the stream busy while `launches` calls are enqueued."""
+        need = 2.0 * launches * host_s + 1e-3
+        torch.cuda._sleep(int(need / max(spin_s_per_cycle, 1e-12)))
+
     start = torch.cuda.Event(enable_timing=True)
     end = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
+    hold(args.steps * n)
     start.record(stream)
     for i in range(args.steps):
-        step(args.warmup + i, evs[i])
+        step(args.warmup + i)
     end.record(stream)
     torch.cuda.synchronize()
     ms_total = start.elapsed_time(end)
     ms_step = ms_total / args.steps
-    call_ms = [np.array([evs[i][j].elapsed_time(evs[i][j + 1]) for i in range(args.steps)])
-               for j in range(n)]
-    per_call_ms = [float(np.mean(v)) for v in call_ms]
+
+    # each call alone: K launches back to back (mean), then K launches each
+    # between its own events (distribution)
+    per_call_ms, call_ms = [], []
+    for j in range(n):
+        for i in range(args.warmup):
+            call(j, args.warmup + i)
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        hold(args.steps)
+        e0.record(stream)
+        for i in range(args.steps):
+            call(j, i)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        per_call_ms.append(e0.elapsed_time(e1) / args.steps)
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(args.steps)]
+        hold(args.steps * 2)
+        for i in range(args.steps):
+            evs[i][0].record(stream)
+            call(j, i)
+            evs[i][1].record(stream)
+        torch.cuda.synchronize()
+        call_ms.append(np.array([a.elapsed_time(b) for a, b in evs]))
 
     calls = []
     for j, (path, T) in enumerate(plan):
@@ -232,6 +285,7 @@ def main():
         p10, p50, p90 = (float(v) for v in np.percentile(call_ms[j], [10, 50, 90]))
         calls.append(dict(path=path, tokens=T, ms=per_call_ms[j], p10_ms=p10, p50_ms=p50,
                           p90_ms=p90, bytes=by, flops=fl, gbs=by / s / 1e9, tflops=fl / s / 1e12))
+        assert q.spear_ec_workspace_status(ws) == 0, "a decode wait gave up during the run"
 
     if args.copy_calibration:
         a = torch.empty(1 << 28, dtype=torch.uint8, device=dev)   # 256 MiB
@@ -251,13 +305,14 @@ def main():
                     "unit": "GB/s", "frac": round(c["gbs"] / HBM_PEAK_GBS, 4),
                     "traffic": traffic.get(f"decode_T{c['tokens']}"),
                     "kernel": f"decode_kernel: the whole decode call ({c['tokens']} tokens) is this one launch",
-                    "avg_us": round(c["ms"] * 1e3, 2)}
+                    "avg_us": round(c["ms"] * 1e3, 2),
+                    "timing": "mean of back-to-back launches between two events on the launch stream"}
         return {"bound": "mfma", "achieved": round(c["tflops"], 1), "peak": BF16_PEAK_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(c["tflops"] / BF16_PEAK_TFLOPS, 4),
                 "traffic": traffic.get(f"prefill_T{c['tokens']}"),
-                "kernel": f"prefill call ({c['tokens']} tokens): projection_kernel + finish_kernel + "
-                          "prefill_kernel, timed together between events on the launch stream",
-                "avg_us": round(c["ms"] * 1e3, 2)}
+                "kernel": f"prefill call ({c['tokens']} tokens): " + PREFILL_KERNELS_TEXT,
+                "avg_us": round(c["ms"] * 1e3, 2),
+                "timing": "mean of back-to-back calls between two events on the launch stream"}
 
     head = dec[0] if dec else pre[0]
     value = head["gbs"] if dec else head["tflops"]
@@ -282,6 +337,7 @@ def main():
         out["prefill"] = {"value": round(pre[0]["tflops"], 2), "unit": "TFLOP/s",
                           "frac_of_peak": round(pre[0]["tflops"] / BF16_PEAK_TFLOPS, 4)}
         out["roofline_decode"] = roof(dec[0])
+    out["host_enqueue_us_per_call"] = round(host_s * 1e6, 1)
     out["kernel_source_hash"] = kernel_source_hash()
     out["setup_s"] = round(setup_s, 1)
 
@@ -328,6 +384,7 @@ def rank_sweep(args):
 
 
 CALIB_BYTES = 1 << 28   # the --copy-calibration copy: 256 MiB read, 256 MiB written
+PREFILL_KERNELS_TEXT = "projection_kernel + finish_kernel + prefill_kernel, timed together"
 
 # Kernels of each call of the dispatcher (matched against the mangled names).
 CALL_KERNELS = {"decode": ("decode_kernel",),
@@ -423,7 +480,14 @@ def cpu_baseline(spec, r, plan, X, A, B, gv, bv, unit, mlp=None, serq=False):
     by = layer_bytes(K, rows, r, g, asym, T, serq)
     fl = layer_flops(K, rows, r, T, serq)
     val = by / secs / 1e9 if unit == "GB/s" else fl / secs / 1e12
+    model = ""
+    try:
+        with open("/proc/cpuinfo") as f:
+            model = next((ln.split(":", 1)[1].strip() for ln in f if ln.startswith("model name")), "")
+    except OSError:
+        pass
     return {"value": round(val, 6), "unit": unit, "cores": 1, "kind": "oracle",
+            "nproc": os.cpu_count(), "cpu_model": model,
             "sample": f"{path} call, all {T} tokens x first {rows} of {N} output rows "
                       f"(compensator for all tokens); forward {secs:.1f} s, quantize {t1 - t0:.1f} s"}
 

@@ -66,6 +66,13 @@ extern "C" {
 /* desc.flags */
 #define SPEAR_EC_ZEROS 1      /* asymmetric codes: `zeros` is present and required */
 #define SPEAR_EC_PER_TENSOR 2 /* one symmetric scale for the whole tensor (stored per row) */
+#define SPEAR_EC_OUT_F32 4    /* diagnostic: y is fp32 [tokens][d_out], the fp32 accumulation
+                                 stored as it is instead of rounded to bf16 (same kernels;
+                                 layer calls only, ignored by the quantizer and dequantizer) */
+
+/* Error bits of a workspace (spear_ec_workspace_status). */
+#define SPEAR_EC_WS_WAIT_TIMEOUT 1 /* a decode workgroup gave up waiting for the gated
+                                      projection; the rows it finished hold NaN */
 
 /* Largest token count the decode path accepts (decode = 1..32 tokens). */
 #define SPEAR_EC_DECODE_MAX_TOKENS 32
@@ -80,7 +87,8 @@ extern "C" {
  *              d_in and no zeros: the symmetric per-tensor format of the
  *              Quasar verify pass, summary "Targeted quantization"; it is
  *              stored as per-channel scales that are all equal, so the layer
- *              calls treat it as per-channel and only the quantizer differs)
+ *              calls treat it as per-channel and only the quantizer differs),
+ *              each optionally with SPEAR_EC_OUT_F32
  * Passed by pointer and read during the call only.
  */
 typedef struct spear_ec_desc {
@@ -102,6 +110,20 @@ typedef struct spear_ec_desc {
  * invalid desc or max_tokens < 0.
  */
 size_t spear_ec_workspace_bytes(const spear_ec_desc* desc, int32_t max_tokens);
+
+/*
+ * Read and clear the error word of a workspace.  The decode kernel never
+ * blocks without bound: where it gives up (a wait for the rank-r projection
+ * that does not end) it writes NaN into the affected outputs and sets a bit
+ * here, and the layer call itself has already returned SPEAR_EC_OK.  This call synchronizes `stream`, stores the
+ * bits seen since the last call (SPEAR_EC_WS_*; 0 = none) in *error_bits and
+ * clears them.  workspace is a device pointer of at least 16 bytes that the
+ * layer calls use; error_bits a host pointer.  Returns SPEAR_EC_OK,
+ * SPEAR_EC_ERR_INVALID_ARGUMENT (NULL pointer), SPEAR_EC_ERR_WORKSPACE
+ * (workspace_bytes < 16) or SPEAR_EC_ERR_HIP.
+ */
+int spear_ec_workspace_status(void* workspace, size_t workspace_bytes, hipStream_t stream,
+                              int32_t* error_bits);
 
 /*
  * Phase-aware dispatch (SPEAR summary, section 2.2 A, phase-aware adaptive

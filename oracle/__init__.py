@@ -40,7 +40,9 @@ def build(force: bool = False) -> str:
 def _load():
     global _lib
     if _lib is None:
-        lib = ctypes.CDLL(build())
+        # SPEAR_ORACLE_LIB: another build of this same source (the sanitizer
+        # test loads one built with AddressSanitizer and UBSan)
+        lib = ctypes.CDLL(os.environ.get("SPEAR_ORACLE_LIB") or build())
         P = ctypes.c_void_p
         i32 = ctypes.c_int
         lib.orc_half_to_double.argtypes = [ctypes.c_uint16]

@@ -8,7 +8,8 @@ holds the kernels (csrc/), their build script (build.py) and a ctypes binding
 to hold device memory and to supply the current stream.
 """
 from .binding import (  # noqa: F401
-    EXPORTED, SPEAR_EC_DECODE_MAX_TOKENS, SPEAR_EC_PER_TENSOR, SPEAR_EC_ZEROS, SpearEcError,
+    EXPORTED, SPEAR_EC_DECODE_MAX_TOKENS, SPEAR_EC_OUT_F32, SPEAR_EC_PER_TENSOR,
+    SPEAR_EC_WS_WAIT_TIMEOUT, SPEAR_EC_ZEROS, SpearEcError,
     load_library, make_desc,
     spear_ec_dequant_f32, spear_ec_desc, spear_ec_last_error, spear_ec_linear,
     spear_ec_linear_decode, spear_ec_linear_mlp_gate, spear_ec_linear_prefill,
@@ -16,6 +17,7 @@ from .binding import (  # noqa: F401
     spear_ec_step_latency_us,
     spear_ec_quantize_rtn,
     spear_ec_status_string, spear_ec_version, spear_ec_workspace_bytes,
+    spear_ec_workspace_status,
 )
 
 

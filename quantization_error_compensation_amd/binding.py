@@ -12,7 +12,9 @@ import ctypes
 import os
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(HERE, "libspear_ec.so")
+# SPEAR_EC_LIB names another build of the library to load (for example a
+# host-only build with sanitizers, used by the CPU tests).
+LIB_PATH = os.environ.get("SPEAR_EC_LIB") or os.path.join(HERE, "libspear_ec.so")
 HEADER = os.path.join(os.path.dirname(HERE), "include", "spear_ec.h")
 
 SPEAR_EC_OK = 0
@@ -23,10 +25,12 @@ SPEAR_EC_ERR_WORKSPACE = 4
 SPEAR_EC_ERR_HIP = 5
 SPEAR_EC_ZEROS = 1
 SPEAR_EC_PER_TENSOR = 2
+SPEAR_EC_OUT_F32 = 4
+SPEAR_EC_WS_WAIT_TIMEOUT = 1
 SPEAR_EC_DECODE_MAX_TOKENS = 32
 
 EXPORTED = (
-    "spear_ec_workspace_bytes", "spear_ec_linear", "spear_ec_linear_decode",
+    "spear_ec_workspace_bytes", "spear_ec_workspace_status", "spear_ec_linear", "spear_ec_linear_decode",
     "spear_ec_linear_prefill", "spear_ec_linear_mlp_gate", "spear_ec_linear_serq",
     "spear_ec_step_latency_us", "spear_ec_pick_chunk", "spear_ec_lut_measure",
     "spear_ec_quantize_rtn",
@@ -66,6 +70,8 @@ def load_library(path: str = LIB_PATH):
     DP = ctypes.POINTER(spear_ec_desc)
     lib.spear_ec_workspace_bytes.argtypes = [DP, i32]
     lib.spear_ec_workspace_bytes.restype = sz
+    lib.spear_ec_workspace_status.argtypes = [P, sz, P, ctypes.POINTER(i32)]
+    lib.spear_ec_workspace_status.restype = ctypes.c_int
     lin = [DP, i32, P, P, P, P, P, P, P, P, ctypes.c_float, P, P, sz, P]
     for name in ("spear_ec_linear", "spear_ec_linear_decode", "spear_ec_linear_prefill"):
         getattr(lib, name).argtypes = lin
@@ -99,8 +105,9 @@ def load_library(path: str = LIB_PATH):
 
 
 def make_desc(d_in: int, d_out: int, rank: int, group_size: int, zeros: bool,
-              per_tensor: bool = False) -> spear_ec_desc:
-    flags = (SPEAR_EC_ZEROS if zeros else 0) | (SPEAR_EC_PER_TENSOR if per_tensor else 0)
+              per_tensor: bool = False, out_f32: bool = False) -> spear_ec_desc:
+    flags = ((SPEAR_EC_ZEROS if zeros else 0) | (SPEAR_EC_PER_TENSOR if per_tensor else 0) |
+             (SPEAR_EC_OUT_F32 if out_f32 else 0))
     return spear_ec_desc(d_in, d_out, rank, group_size, flags)
 
 
@@ -142,6 +149,16 @@ def spear_ec_last_error() -> str:
 
 def spear_ec_workspace_bytes(desc: spear_ec_desc, max_tokens: int) -> int:
     return int(load_library().spear_ec_workspace_bytes(ctypes.byref(desc), int(max_tokens)))
+
+
+def spear_ec_workspace_status(workspace, stream=None) -> int:
+    """Synchronize the stream, return the workspace's error bits
+    (SPEAR_EC_WS_*, 0 = none) and clear them."""
+    bits = ctypes.c_int32(0)
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check(load_library().spear_ec_workspace_status(_ptr(workspace), ws_bytes, _stream(stream),
+                                                    ctypes.byref(bits)))
+    return int(bits.value)
 
 
 def _linear(name, desc, x, wq, scales, zeros, A, B, g, b, alpha, y, workspace, stream):

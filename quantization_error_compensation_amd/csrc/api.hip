@@ -32,30 +32,10 @@ DecodePlan plan_decode(const Shape& s, int slots) {
   const int KB = s.KB();
   pl.bands = (s.N + kDecodeBandRows - 1) / kDecodeBandRows;
   pl.rank_bands = s.serq ? 0 : (s.r + 63) / 64;  // SERQ takes x's channels, no projection
-  pl.units = (pl.bands + pl.rank_bands) * KB;
-  // Costs in KB moved: a row unit is kDecodeBandRows x 64 B of codes, a rank
-  // unit 64 x 256 B of A, costed 1.25 times that so the rank bands, which
-  // every row finisher waits for, complete early.  A rank unit is costed as
-  // a full band whatever r is: its time (x, the barrier and four tiles of
-  // matrix-core work per block) hardly depends on how many ranks it holds.
-  pl.row_cost = kDecodeBandRows / 16;
-  pl.rank_cost = 20;
-  pl.cost = (long long)pl.rank_bands * KB * pl.rank_cost + (long long)pl.bands * KB * pl.row_cost;
-  // At least twice the dearest unit per workgroup: a run of cost C >= that
-  // unit's cost always holds a unit, which the kernel's count of the
-  // workgroups sharing a band relies on (and a run whose start moves to an
-  // even block keeps one).
-  const int umax = pl.rank_bands > 0 ? std::max(pl.row_cost, pl.rank_cost) : pl.row_cost;
-  auto wgs = [&](int sl) {
-    long long P = std::min<long long>(sl, std::max<long long>(1, pl.cost / (2 * umax)));
-    return (int)std::max<long long>(1, std::min<long long>(P, pl.units));
-  };
-  pl.workgroups = wgs(std::min(std::max(slots, 1), kMaxSlots));
-  // A band of cost Cb meets at most ceil(Cb * P / cost) + 1 workgroup runs;
-  // the bound grows with P, so the workspace is sized for the largest P.
-  const long long pmax = wgs(kMaxSlots);
-  const long long cb = (long long)KB * umax;
-  pl.maxseg = (int)std::min<long long>(pmax, (cb * pmax + pl.cost - 1) / pl.cost + 1);
+  slots = std::min(std::max(slots, 1), kMaxSlots);
+  pl.split = make_split(KB, pl.rank_bands, pl.bands, slots);
+  pl.workgroups = pl.split.P;
+  pl.slots = split_workspace_slots(KB, pl.rank_bands, pl.bands, kMaxSlots);
   return pl;
 }
 
@@ -101,8 +81,7 @@ Workspace layout(const Shape& s, bool decode) {
     w.wvhi = w.wvlo = w.sblk = w.stot = w.upart = o;
     w.ypart = o;
     const size_t T4 = (T + 3) & ~(size_t)3;  // tokens rounded up to a multiple of 4
-    o = up256(o + sizeof(float) * (size_t)(dp.bands + dp.rank_bands) * dp.maxseg * T4 *
-                       kDecodeBandRows);
+    o = up256(o + sizeof(float) * (size_t)dp.slots * T4 * kDecodeBandRows);
   } else {
     const ProjPlan pp = plan_projection(s);
     const size_t Tp = (size_t)pp.tiles * kProjTokens;
@@ -143,7 +122,7 @@ static int check_desc(const spear_ec_desc* d, bool need_rank) {
   if (!d) return fail(SPEAR_EC_ERR_INVALID_ARGUMENT, "desc is NULL");
   if (d->d_in <= 0 || d->d_out <= 0 || d->rank < 0 || d->group_size <= 0)
     return fail(SPEAR_EC_ERR_INVALID_ARGUMENT, "desc has a non-positive size");
-  if (d->flags & ~(SPEAR_EC_ZEROS | SPEAR_EC_PER_TENSOR))
+  if (d->flags & ~(SPEAR_EC_ZEROS | SPEAR_EC_PER_TENSOR | SPEAR_EC_OUT_F32))
     return fail(SPEAR_EC_ERR_INVALID_ARGUMENT, "unknown desc.flags bits");
   if ((d->flags & SPEAR_EC_PER_TENSOR) && ((d->flags & SPEAR_EC_ZEROS) || d->group_size != d->d_in))
     return fail(SPEAR_EC_ERR_UNSUPPORTED, "SPEAR_EC_PER_TENSOR needs group_size == d_in and no zeros");
@@ -235,6 +214,7 @@ static int linear(Path path, const spear_ec_desc* d, int32_t tokens, const void*
   a.b2 = gmlp ? mlp.b2 : nullptr;
   a.alpha = alpha;
   a.y = y;
+  a.out_f32 = (d->flags & SPEAR_EC_OUT_F32) != 0;
   const WsPtrs wp = carve(workspace, wl);
   if (decode) return hip_status(launch_decode(s, a, wp, stream), "decode kernel launch");
   rc = hip_status(launch_projection(s, a, wp, stream), "projection kernel launch");
@@ -284,6 +264,7 @@ static int linear_serq(const spear_ec_desc* d, int32_t tokens, const void* x, co
   a.alpha = 1.f;
   a.y = y;
   a.s0 = s0;
+  a.out_f32 = (d->flags & SPEAR_EC_OUT_F32) != 0;
   const WsPtrs wp = carve(workspace, wl);
   if (decode) return hip_status(launch_decode(s, a, wp, stream), "decode kernel launch");
   Shape s_sums = s;  // the block sums of x only
@@ -318,6 +299,26 @@ size_t spear_ec_workspace_bytes(const spear_ec_desc* desc, int32_t max_tokens) {
   }
   if (need == 0) need = layout(make_shape(desc, 1), false).total;
   return need;
+}
+
+int spear_ec_workspace_status(void* workspace, size_t workspace_bytes, hipStream_t stream,
+                              int32_t* error_bits) {
+  g_last_error[0] = 0;
+  if (!workspace || !error_bits)
+    return fail(SPEAR_EC_ERR_INVALID_ARGUMENT, "workspace and error_bits are required");
+  if (workspace_bytes < sizeof(int32_t) * (kCtrError + 1))
+    return fail(SPEAR_EC_ERR_WORKSPACE, "workspace is smaller than its counter words");
+  int32_t* word = static_cast<int32_t*>(workspace) + kCtrError;
+  int32_t bits = 0;
+  int rc = hip_status(hipStreamSynchronize(stream), "stream synchronize");
+  if (!rc) rc = hip_status(hipMemcpy(&bits, word, sizeof(bits), hipMemcpyDeviceToHost),
+                           "error word read");
+  if (!rc && bits) {
+    const int32_t zero = 0;
+    rc = hip_status(hipMemcpy(word, &zero, sizeof(zero), hipMemcpyHostToDevice), "error word clear");
+  }
+  if (!rc) *error_bits = bits;
+  return rc;
 }
 
 int spear_ec_linear(const spear_ec_desc* desc, int32_t tokens, const void* x, const uint32_t* wq,

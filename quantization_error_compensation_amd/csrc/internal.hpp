@@ -6,6 +6,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include "partition.hpp"
+
 namespace spear {
 
 constexpr int kBlockK = 128;          // K block: one scale group (g = 128) or a slice of a row
@@ -22,11 +24,11 @@ constexpr int kCounterSlots = 4096;   // int32 words at the head of the workspac
 // Decode counter words (all zero between calls).
 constexpr int kCtrRankDone = 1;  // rank bands whose gated projection is published
 constexpr int kCtrExit = 2;      // decode workgroups that have finished
-constexpr int kCtrError = 3;     // set to 1 if a workgroup saw an inconsistent workspace
+constexpr int kCtrError = 3;     // error bits (SPEAR_EC_WS_*), read and cleared by the host
 constexpr int kCtrGateDone = 4;  // MLP gate: 1 once alpha * v of every rank is published
 constexpr int kCtrBand = 64;       // [64, 64 + bands): arrivals per band (rank bands first)
 constexpr int kCtrTile = 64;       // [64, 64 + tiles): prefill split-K arrivals per output tile
-constexpr int kMaxSlots = 1024;    // bound on resident decode workgroups used for sizing
+constexpr int kMaxSlots = 256;     // bound on decode workgroups (one per compute unit of gfx950)
 
 struct Shape {
   int K, N, r, g, T;
@@ -42,17 +44,14 @@ struct ProjPlan {
   int splits;  // K splits
 };
 
-// Work split of the fused decode kernel (stream-K over band x block units).
+// Work split of the fused decode kernel (rank units spread over the first
+// workgroups, stream-K over the row units; partition.hpp).
 struct DecodePlan {
-  int bands;       // output bands of kDecodeBandRows rows
-  int rank_bands;  // 64-rank bands of A
-  int units;       // (bands + rank_bands) * K/128
-  int row_cost;    // cost of one row unit (its KB of codes)
-  int rank_cost;   // cost of one rank unit (1.25 x the KB of a full 64-rank band)
-  long long cost;  // total cost of all units
-  int workgroups;  // persistent workgroups, each a run of units of equal cost
-  int maxseg;      // bound on the partial sums of one band (any P up to kMaxSlots): the
-                   // workgroups sharing it
+  int bands;         // output bands of kDecodeBandRows rows
+  int rank_bands;    // 64-rank bands of A
+  DecodeSplit split;
+  int workgroups;    // persistent workgroups (split.P)
+  int slots;         // partial-sum slots the workspace holds (for any slots <= kMaxSlots)
 };
 
 // Work split of the prefill GEMM: output tiles of kPrefillBM x kPrefillBN,
@@ -65,7 +64,7 @@ struct PrefillPlan {
 
 ProjPlan plan_projection(const Shape& s);
 PrefillPlan plan_prefill(const Shape& s);
-// slots: workgroups the device keeps resident (2 per CU); sizing uses kMaxSlots.
+// slots: workgroups the device keeps resident (one per CU); sizing uses kMaxSlots.
 DecodePlan plan_decode(const Shape& s, int slots);
 
 // Byte offsets of the workspace regions for one call.
@@ -83,7 +82,7 @@ struct WsPtrs {
   uint32_t* sblk;  // [KB][Tp][2] sum of x over each 128-column block as bf16 hi|mid, lo (prefill)
   float* stot;     // [T]         sum of x over the whole row (prefill)
   float* upart;    // projection partials: prefill [splits][T][r+1], decode [splits][T][r]
-  float* ypart;    // decode: [bands][maxseg][64][T4] (T4: T rounded up to 4); prefill: split-K tile partials
+  float* ypart;    // decode: [slots][128 columns][T4] (T4: T rounded up to 4); prefill: split-K tile partials
 };
 WsPtrs carve(void* base, const Workspace& w);
 
@@ -108,6 +107,8 @@ struct LayerArgs {
   // SERQ (s0 >= 0): the correction is x[:, s0 .. s0 + r) R^T with R in B's
   // place (no A, no gate, alpha 1)
   int s0 = -1;
+  // y is fp32 (the accumulation stored unrounded) instead of bf16
+  bool out_f32 = false;
 };
 
 hipError_t launch_projection(const Shape& s, const LayerArgs& a, const WsPtrs& w,

@@ -8,13 +8,15 @@
 //
 // Work.  A "band" is either BR = 16 x (waves per workgroup) output rows of
 // packed codes or 64 rows (ranks) of A; a "unit" is one 128-column block of
-// one band.  Rank bands come first in the unit order.  Units carry a cost
-// (the KB they move, 1.25 times that for rank units) and the P persistent
-// workgroups each take a contiguous run of units of equal cost (stream-K).  A workgroup walks
-// its run band segment by band segment.  A band covered by several
-// workgroups has its partial sums combined by whichever arrives last (in
-// segment order, so results are deterministic); partial sums move through
-// device-scope stores and loads (coherent across XCDs, no L2-wide fence).
+// one band.  partition.hpp fixes which units each of the P persistent
+// workgroups takes: the rank units in short runs on the first workgroups
+// (so the projection every row finisher needs is published early), and the
+// row units in a stream-K split in which those workgroups' share starts later
+// by the cost of their rank units.  A workgroup walks its runs band segment
+// by band segment.  A band covered by several workgroups has its partial sums
+// combined by whichever arrives last (in workgroup order, so results are
+// deterministic); partial sums move through device-scope stores and loads
+// (coherent across XCDs, no L2-wide fence).
 //
 // Inside a row segment each wave of a workgroup owns one 16-row tile and all
 // walk the same K blocks in bursts of NS blocks (tall bands and short bursts:
@@ -39,10 +41,11 @@
 // (v split into bf16 high and low parts) and stores y.
 //
 // Waiting: finishers of row bands wait for the rank bands to publish.  Rank
-// units are the first units, owned by the lowest workgroup indices, which the
-// dispatcher starts first, so they run before anyone waits; rank units are
-// costed above their byte count so those workgroups finish early.  The wait
-// is bounded and raises an error word instead of hanging.
+// units belong to the lowest workgroup indices, which the dispatcher starts
+// first; a rank workgroup never waits before it has published its share, so
+// the waits end whenever those workgroups get compute units.  The wait is
+// bounded all the same: one that gives up writes NaN and sets an error bit
+// (spear_ec_workspace_status).
 #include "common.hpp"
 #include "internal.hpp"
 
@@ -64,21 +67,18 @@ struct DecodeParams {
   const float* w2;         // [r][gh]
   const float* b2;         // [r]
   float alpha;
-  float* part;             // [bands][maxseg][BR][T4] partial sums
+  float* part;             // [nslots][BR][T4] partial sums
   float* wv32;             // [T][r] alpha * v
   int* ctr;                // counter words
-  uint16_t* y;             // [T][N] bf16
+  void* y;                 // [T][N] bf16 (fp32 with out_f32)
+  int out_f32;
   int T, K, N, r, G, ZW, has_z;
   int KB;                  // 128-column blocks per row
   int RB;                  // rank bands (64 ranks each)
-  int NB;                  // row bands (BR rows each)
-  int P;                   // workgroups
-  int row_cost;            // cost of a row unit
-  int rank_cost;           // cost of a rank unit
-  long long ctot;          // total cost of all units
+  DecodeSplit sp;          // which units each workgroup takes (partition.hpp)
+  int nslots;              // partial-sum slots in the workspace
   int s0;                  // SERQ: first salient channel (the correction is x[:, s0 ..] R^T,
                            // R in B's place, no rank bands); -1 otherwise
-  int maxseg;              // bound on the partial sums of one band
 };
 
 constexpr int W = kDecodeWaves;        // waves per workgroup
@@ -88,7 +88,9 @@ static_assert(W == 8 || W == 16, "a workgroup is 8 or 16 waves");
 constexpr int kThreads = 64 * W;
 
 constexpr int XROW = 272;            // LDS row of one token: 256 B + 16 B pad
-constexpr int kSpinLimit = 1 << 20;  // bounded wait (about a second)
+// Bounded wait: 2^20 polls, each a device-scope load (about a microsecond
+// under load) after s_sleep 1 (64 clocks): about a second at most.
+constexpr int kSpinLimit = 1 << 20;
 
 // Blocks per burst: 4 in row segments up to 16 tokens (2 above, for
 // registers), one per phase in rank segments.  One
@@ -102,36 +104,6 @@ struct Burst {
   static constexpr int kSums = kMax * 16 * MT * XROW;  // byte offset of the block sums
   static constexpr int kBuf = kSums + kMax * 16 * MT * 4;  // bytes of one x buffer
 };
-
-// ------------------------------------------------------------- partition
-// Cost of the first u units, and the first unit of workgroup w: the smallest
-// u with S(u) * P >= w * ctot (moved to an even block of a row band).
-// owner_of(u) is the workgroup whose run holds unit u.
-__device__ __forceinline__ long long cost_prefix(const DecodeParams& p, long long u) {
-  const long long ru = (long long)p.RB * p.KB;
-  return u <= ru ? u * p.rank_cost : ru * p.rank_cost + (u - ru) * p.row_cost;
-}
-__device__ __forceinline__ long long unit_begin_exact(const DecodeParams& p, int w) {
-  const long long X = (long long)w * p.ctot;
-  const long long ru = (long long)p.RB * p.KB;
-  const long long rc = (long long)p.rank_cost * p.P;
-  const long long wc = (long long)p.row_cost * p.P;
-  if (X <= ru * rc) return (X + rc - 1) / rc;
-  return ru + (X - ru * rc + wc - 1) / wc;
-}
-// Runs start at an even block of a row band, so the bursts' code loads stay
-// aligned to 128-byte lines: a start at an odd offset moves one unit on (a
-// run keeps at least one unit, since it costs at least two of the dearest).
-__device__ __forceinline__ long long unit_begin(const DecodeParams& p, int w) {
-  long long u = unit_begin_exact(p, w);
-  const long long ru = (long long)p.RB * p.KB;
-  if (u > ru && u < ru + (long long)p.NB * p.KB && ((u - ru) % p.KB) % 2 == 1) ++u;
-  return u;
-}
-__device__ __forceinline__ int owner_of(const DecodeParams& p, long long u) {
-  const int o = (int)(cost_prefix(p, u) * p.P / p.ctot);
-  return u == unit_begin_exact(p, o) && unit_begin(p, o) != u ? o - 1 : o;  // moved start
-}
 
 // ------------------------------------------------------------- x staging
 // x of blocks [b, b + NS) into an LDS buffer [NS][16*MT tokens][XROW], each
@@ -518,49 +490,54 @@ __device__ void row_segment(const DecodeParams& p, int band, int lo, int hi, uin
 }
 
 // ------------------------------------------------------------ partial sums
-// [maxseg][BR columns][T4] floats per band (T4: T rounded up to a multiple
-// of 4), written and read at device scope; a lane's four tokens of one
-// column form one 16-byte word, and words holding no token below T are
-// neither stored nor loaded.  Column c of a partial is row BR band + c of a
-// row band, or rank 64 rb + c (c < 64) of a rank band.
+// [nslots][BR columns][T4] floats (T4: T rounded up to a multiple of 4),
+// written and read at device scope; a lane's four tokens of one column form
+// one 16-byte word, and words holding no token below T are neither stored
+// nor loaded.  Column c of a partial is row BR band + c of a row band, or
+// rank 64 rb + c (c < 64) of a rank band.  The slot of workgroup w's partial
+// of a band is fixed by the split (row_slot, rank_slot).
 __device__ __forceinline__ int tokens4(const DecodeParams& p) { return (p.T + 3) & ~3; }
-__device__ __forceinline__ rsrc_t part_rsrc(const DecodeParams& p, int band) {
-  const uint32_t seg = (uint32_t)BR * tokens4(p);  // floats of one partial
-  return make_rsrc(p.part + (size_t)band * p.maxseg * seg, (uint32_t)p.maxseg * seg * 4);
+__device__ __forceinline__ rsrc_t part_rsrc(const DecodeParams& p) {
+  return make_rsrc(p.part, (uint32_t)p.nslots * BR * tokens4(p) * 4);
 }
-__device__ __forceinline__ uint32_t part_off(const DecodeParams& p, int sidx, int col, int t) {
-  return (uint32_t)(((sidx * BR + col) * tokens4(p) + t) * 4);
+__device__ __forceinline__ uint32_t part_off(const DecodeParams& p, int slot, int col, int t) {
+  return (uint32_t)(((slot * BR + col) * tokens4(p) + t) * 4);
+}
+__device__ __forceinline__ int slot_of(const DecodeParams& p, bool rank, int w, int band) {
+  return rank ? rank_slot(p.sp, w, band) : row_slot(p.sp, w, band);
 }
 
 template <int MT>
-__device__ __forceinline__ void put_part(const DecodeParams& p, int band, int sidx, int col,
+__device__ __forceinline__ void put_part(const DecodeParams& p, int slot, int col,
                                          const f32x4 (&v)[MT]) {
   const int q = (threadIdx.x & 63) >> 4;
-  const rsrc_t r = part_rsrc(p, band);
+  const rsrc_t r = part_rsrc(p);
   for (int mt = 0; mt < MT; ++mt) {
     const int t = 16 * mt + 4 * q;
-    if (t < p.T) bstore16_dev(r, part_off(p, sidx, col, t), 0, v[mt]);
+    if (t < p.T) bstore16_dev(r, part_off(p, slot, col, t), 0, v[mt]);
   }
 }
 
-// The band's nseg partials summed in segment order; 8 / MT partials are in
-// flight at a time.
+// The partials of workgroups first .. first + nseg - 1 for one band, summed
+// in workgroup order; 16 / MT partials are in flight at a time.
 template <int MT>
-__device__ __forceinline__ void sum_parts(const DecodeParams& p, int band, int nseg, int col,
-                                          f32x4 (&v)[MT]) {
-  constexpr int CH = 8 / MT;
+__device__ __forceinline__ void sum_parts(const DecodeParams& p, bool rank, int band, int first,
+                                          int nseg, int col, f32x4 (&v)[MT]) {
+  constexpr int CH = 16 / MT;
   const int q = (threadIdx.x & 63) >> 4;
-  const rsrc_t r = part_rsrc(p, band);
+  const rsrc_t r = part_rsrc(p);
   for (int mt = 0; mt < MT; ++mt) v[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
   for (int k0 = 0; k0 < nseg; k0 += CH) {
     const int n = min(CH, nseg - k0);
     u32x4 w[CH][MT];
-    for (int kk = 0; kk < CH; ++kk)
+    for (int kk = 0; kk < CH; ++kk) {
+      const int slot = kk < n ? slot_of(p, rank, first + k0 + kk, band) : 0;
       for (int mt = 0; mt < MT; ++mt) {
         const int t = 16 * mt + 4 * q;
-        w[kk][mt] = kk < n && t < p.T ? bload16_dev(r, part_off(p, k0 + kk, col, t), 0)
+        w[kk][mt] = kk < n && t < p.T ? bload16_dev(r, part_off(p, slot, col, t), 0)
                                       : u32x4{0u, 0u, 0u, 0u};
       }
+    }
     for (int kk = 0; kk < CH; ++kk)
       if (kk < n)
         for (int mt = 0; mt < MT; ++mt) v[mt] += __builtin_bit_cast(f32x4, w[kk][mt]);
@@ -651,22 +628,29 @@ __device__ void gate_mlp(const DecodeParams& p, uint8_t* lds, int lds_floats) {
   __syncthreads();  // the LDS is the caller's again
 }
 
-// Wait (bounded, error word on timeout) until alpha * v of every rank is
-// published: every rank band (elementwise gate) or the MLP gate's pass.
-__device__ __forceinline__ void wait_ranks(const DecodeParams& p) {
+// Wait (bounded) until alpha * v of every rank is published: every rank band
+// (elementwise gate) or the MLP gate's pass.  Returns false for the whole
+// workgroup if the wait gave up; the error word then has
+// SPEAR_EC_WS_WAIT_TIMEOUT (1) set.
+__device__ __forceinline__ bool wait_ranks(const DecodeParams& p, int* s_flag) {
   if (threadIdx.x == 0) {
-    int spins = 0;
+    int spins = 0, ok = 1;
     const int* ctr = p.gh > 0 ? &p.ctr[kCtrGateDone] : &p.ctr[kCtrRankDone];
     const int target = p.gh > 0 ? 1 : p.RB;
     while (load_dev(ctr) < target) {
       __builtin_amdgcn_s_sleep(1);
       if (++spins > kSpinLimit) {
         atomicOr(&p.ctr[kCtrError], 1);
+        ok = 0;
         break;
       }
     }
+    *s_flag = ok;
   }
   __syncthreads();
+  const bool ok = *s_flag != 0;
+  __syncthreads();
+  return ok;
 }
 
 // alpha * v of this lane's tokens as matrix-core operands: for each K = 32
@@ -752,7 +736,8 @@ __device__ __forceinline__ void add_correction(const DecodeParams& p, const u32x
   }
 }
 
-// Store y for this wave's tile of a finished row band.
+// Store y for this wave's tile of a finished row band (bf16, or fp32 with
+// out_f32).
 template <int MT>
 __device__ __forceinline__ void store_row(const DecodeParams& p, int band, const f32x4 (&yv)[MT]) {
   const int lane = threadIdx.x & 63, wave = wave_id(), q = lane >> 4, c16 = lane & 15;
@@ -761,27 +746,30 @@ __device__ __forceinline__ void store_row(const DecodeParams& p, int band, const
     for (int mt = 0; mt < MT; ++mt)
       for (int i = 0; i < 4; ++i) {
         const int t = 16 * mt + 4 * q + i;
-        if (t < p.T) p.y[(size_t)t * p.N + nrow] = (uint16_t)f32_to_bf16_rne(yv[mt][i]);
+        if (t >= p.T) continue;
+        if (p.out_f32) static_cast<float*>(p.y)[(size_t)t * p.N + nrow] = yv[mt][i];
+        else static_cast<uint16_t*>(p.y)[(size_t)t * p.N + nrow] = (uint16_t)f32_to_bf16_rne(yv[mt][i]);
       }
 }
 
-// Add a partial sum to a band (slot sidx of nparts) and report whether this
-// workgroup arrived last; the last one gets the sum of all partials in slot
-// order in v and clears the band's counter.  Waves with act false (those
-// past the 64 columns of a rank band) hold no column.
+// Add this workgroup's partial sum of a band (shared by workgroups first ..
+// first + nseg - 1) and report whether it arrived last; the last one gets
+// the sum of all partials in workgroup order in v and clears the band's
+// counter (counter cband).  Waves with act false (those past the 64 columns
+// of a rank band) hold no column.
 template <int MT>
-__device__ __forceinline__ bool arrive(const DecodeParams& p, int band, int sidx, int nparts,
-                                       bool act, int* s_last, f32x4 (&v)[MT]) {
+__device__ __forceinline__ bool arrive(const DecodeParams& p, bool rank, int band, int cband,
+                                       int first, int nseg, bool act, int* s_last, f32x4 (&v)[MT]) {
   const int tid = threadIdx.x, col = 16 * wave_id() + (tid & 15);
-  if (act) put_part<MT>(p, band, sidx, col, v);
+  if (act) put_part<MT>(p, slot_of(p, rank, blockIdx.x, band), col, v);
   wait_vmem();
   __syncthreads();
-  if (tid == 0) *s_last = atomicAdd(&p.ctr[kCtrBand + band], 1) == nparts - 1;
+  if (tid == 0) *s_last = atomicAdd(&p.ctr[kCtrBand + cband], 1) == nseg - 1;
   __syncthreads();
   const bool last = *s_last;
   if (last) {
-    if (act) sum_parts<MT>(p, band, nparts, col, v);
-    if (tid == 0) store_dev(&p.ctr[kCtrBand + band], 0);
+    if (act) sum_parts<MT>(p, rank, band, first, nseg, col, v);
+    if (tid == 0) store_dev(&p.ctr[kCtrBand + cband], 0);
   }
   return last;
 }
@@ -795,35 +783,34 @@ __global__ __launch_bounds__(kThreads, W * kDecodeOccupancy / 4) void decode_ker
   static_assert(2 * Burst<MT>::kBuf / 4 >= 16 * MT * 256 + 128, "MLP gate LDS");
   __shared__ __attribute__((aligned(16))) uint8_t xlds[2 * Burst<MT>::kBuf];
   __shared__ __attribute__((aligned(16))) uint8_t mlds[GROUPED ? W * Meta<MT>::kWave : 16];
-  __shared__ int s_last;
+  __shared__ int s_last, s_wait;
   const int tid = threadIdx.x;
   const int wg = blockIdx.x;
-  const long long u0 = unit_begin(p, wg), u1 = unit_begin(p, wg + 1);
+  const DecodeSplit& sp = p.sp;
   int burst = 0;
 
-  for (long long u = u0; u < u1;) {
-    const int band = (int)(u / p.KB);
-    const long long bbeg = (long long)band * p.KB, bend = bbeg + p.KB;
-    const int lo = (int)(u - bbeg);
-    const int hi = (int)(min(u1, bend) - bbeg);
-    u = min(u1, bend);
-    const int first = owner_of(p, bbeg);
-    const int nseg = owner_of(p, bend - 1) - first + 1;
-    const int sidx = wg - first;
-    const bool rank = band < p.RB;
-    const int nparts = nseg;
-    if (nparts > p.maxseg) {  // cannot happen with a workspace sized by the planner
-      if (tid == 0) atomicOr(&p.ctr[kCtrError], 2);
-      continue;
-    }
+  // Rank units first (workgroups below sp.Rw), then row units.
+  for (int pass = 0; pass < 2; ++pass) {
+    const bool rank = pass == 0;
+    const uint32_t u0 = rank ? rank_begin(sp, wg) : row_begin(sp, wg);
+    const uint32_t u1 = rank ? rank_begin(sp, wg + 1) : row_begin(sp, wg + 1);
+    for (uint32_t u = u0; u < u1;) {
+      const int band = (int)(u / (uint32_t)p.KB);  // rank band, or row band
+      const uint32_t bbeg = (uint32_t)band * p.KB, bend = bbeg + p.KB;
+      const int lo = (int)(u - bbeg);
+      const int hi = (int)(min(u1, bend) - bbeg);
+      u = min(u1, bend);
+      const int first = rank ? rank_owner(sp, bbeg) : row_owner(sp, bbeg);
+      const int nseg = (rank ? rank_owner(sp, bend - 1) : row_owner(sp, bend - 1)) - first + 1;
+      const int cband = rank ? band : p.RB + band;  // arrival counter
 
-    f32x4 v[MT];
-    if (rank) rank_segment<MT>(p, band, lo, hi, xlds, burst, v);
-    else row_segment<MT, GROUPED>(p, band - p.RB, lo, hi, xlds, mlds, burst, v);
+      f32x4 v[MT];
+      if (rank) rank_segment<MT>(p, band, lo, hi, xlds, burst, v);
+      else row_segment<MT, GROUPED>(p, band, lo, hi, xlds, mlds, burst, v);
 
-    const bool fin = nparts == 1 || arrive<MT>(p, band, sidx, nparts, !rank || wave_id() < 4,
-                                               &s_last, v);
-    if (fin) {
+      const bool fin = nseg == 1 || arrive<MT>(p, rank, band, cband, first, nseg,
+                                               !rank || wave_id() < 4, &s_last, v);
+      if (!fin) continue;
       if (rank) {
         finish_rank<MT>(p, band, v);
         wait_vmem();
@@ -834,26 +821,29 @@ __global__ __launch_bounds__(kThreads, W * kDecodeOccupancy / 4) void decode_ker
       } else {
         if (p.r > 0) {
           u32x4 bfr[kRankSteps];
-          b_fragments(p, band - p.RB, bfr);
+          b_fragments(p, band, bfr);
           u32x4 vhi[kRankSteps][MT], vlo[kRankSteps][MT];
           if (p.s0 >= 0) {  // SERQ: x's salient channels, nothing to wait for
             serq_operands<MT>(p, vhi);
             for (int k = 0; k < kRankSteps; ++k)
               for (int mt = 0; mt < MT; ++mt) vlo[k][mt] = u32x4{0u, 0u, 0u, 0u};
-          } else {
-            wait_ranks(p);
+          } else if (wait_ranks(p, &s_wait)) {
             alpha_v_operands<MT>(p, vhi, vlo);
+          } else {  // gave up waiting: no plausible-looking output
+            for (int mt = 0; mt < MT; ++mt) v[mt] = f32x4{NAN, NAN, NAN, NAN};
+            for (int k = 0; k < kRankSteps; ++k)
+              for (int mt = 0; mt < MT; ++mt) vhi[k][mt] = vlo[k][mt] = u32x4{0u, 0u, 0u, 0u};
           }
           add_correction<MT>(p, bfr, vhi, vlo, v);
         }
-        store_row<MT>(p, band - p.RB, v);
+        store_row<MT>(p, band, v);
       }
     }
   }
 
   if (p.RB > 0 && tid == 0) {
     wait_vmem();
-    if (atomicAdd(&p.ctr[kCtrExit], 1) == p.P - 1) {
+    if (atomicAdd(&p.ctr[kCtrExit], 1) == sp.P - 1) {
       store_dev(&p.ctr[kCtrRankDone], 0);
       store_dev(&p.ctr[kCtrGateDone], 0);
       store_dev(&p.ctr[kCtrExit], 0);
@@ -863,7 +853,7 @@ __global__ __launch_bounds__(kThreads, W * kDecodeOccupancy / 4) void decode_ker
 
 template <int MT, bool GROUPED>
 hipError_t go(const DecodeParams& p, hipStream_t st) {
-  hipLaunchKernelGGL((decode_kernel<MT, GROUPED>), dim3(p.P), dim3(kThreads), 0, st, p);
+  hipLaunchKernelGGL((decode_kernel<MT, GROUPED>), dim3(p.sp.P), dim3(kThreads), 0, st, p);
   return hipGetLastError();
 }
 
@@ -905,7 +895,8 @@ hipError_t launch_decode(const Shape& s, const LayerArgs& a, const WsPtrs& w, hi
   p.part = w.ypart;
   p.wv32 = w.wv32;
   p.ctr = w.counters;
-  p.y = static_cast<uint16_t*>(a.y);
+  p.y = a.y;
+  p.out_f32 = a.out_f32 ? 1 : 0;
   p.T = s.T;
   p.K = s.K;
   p.N = s.N;
@@ -914,12 +905,8 @@ hipError_t launch_decode(const Shape& s, const LayerArgs& a, const WsPtrs& w, hi
   p.ZW = (p.G + 7) / 8;
   p.KB = s.KB();
   p.RB = pl.rank_bands;
-  p.NB = pl.bands;
-  p.P = pl.workgroups;
-  p.row_cost = pl.row_cost;
-  p.rank_cost = pl.rank_cost;
-  p.ctot = pl.cost;
-  p.maxseg = pl.maxseg;
+  p.sp = pl.split;
+  p.nslots = pl.slots;
   p.s0 = a.s0;
   if (s.T <= 16) return s.grouped ? go<1, true>(p, st) : go<1, false>(p, st);
   return s.grouped ? go<2, true>(p, st) : go<2, false>(p, st);

@@ -56,8 +56,8 @@ struct PrefillParams {
   const float* stot;       // [T]
   float* part;             // [tiles][splits][8 waves][64 values][64 lanes] split partials
   int* ctr;                // counter words
-  uint16_t* y;             // [T][N]
-  int T, K, N, r, Tp, G, ZW, has_z, tiles_m, tiles_n, splits;
+  void* y;                 // [T][N] bf16 (fp32 with out_f32)
+  int T, K, N, r, Tp, G, ZW, has_z, tiles_m, tiles_n, splits, out_f32;
 };
 
 constexpr int kXStage = kPrefillBM * 256;  // 32 KB
@@ -310,7 +310,9 @@ __global__ __launch_bounds__(512, 1) void prefill_kernel(PrefillParams p) {
       if (n >= p.N) continue;
       for (int v = 0; v < 16; ++v) {
         const int t = m0 + wm * 64 + ms * 32 + 8 * (v >> 2) + 4 * q + (v & 3);
-        if (t < p.T) p.y[(size_t)t * p.N + n] = (uint16_t)f32_to_bf16_rne(tot[ms][ns][v]);
+        if (t >= p.T) continue;
+        if (p.out_f32) static_cast<float*>(p.y)[(size_t)t * p.N + n] = tot[ms][ns][v];
+        else static_cast<uint16_t*>(p.y)[(size_t)t * p.N + n] = (uint16_t)f32_to_bf16_rne(tot[ms][ns][v]);
       }
     }
 }
@@ -333,7 +335,8 @@ hipError_t launch_prefill(const Shape& s, const LayerArgs& a, const WsPtrs& w, h
   p.stot = w.stot;
   p.part = w.ypart;
   p.ctr = w.counters;
-  p.y = static_cast<uint16_t*>(a.y);
+  p.y = a.y;
+  p.out_f32 = a.out_f32 ? 1 : 0;
   p.T = s.T;
   p.K = s.K;
   p.N = s.N;

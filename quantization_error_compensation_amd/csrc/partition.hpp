@@ -1,0 +1,180 @@
+// Work split of the decode kernel: which rank units (128-column blocks of
+// 64 rows of A) and which row units (128-column blocks of one row band) each
+// persistent workgroup takes.  The same functions run in the kernel and on
+// the host (the planner, and a host-built check over a grid of shapes).
+//
+// Units.  Rank units are numbered band-major, [0, RU) with RU = RB * KB; row
+// units the same, [0, WU) with WU = NB * KB.
+//
+// Rank units.  Workgroups [0, Rw) take contiguous, near-equal runs of the
+// rank units, rank_begin(w) = floor(w RU / Rw), so the rank-r projection is
+// spread over many compute units and is published early (every row band's
+// finisher waits for it).
+//
+// Row units.  Laid out as a stream-K split over a cost axis of C row-unit
+// equivalents: workgroup w owns [w C / P', (w + 1) C / P') (P' = P - S, w
+// counted from S), and a rank workgroup spends the first D units of its
+// range on its rank units ("shared" mode, S = 0: rank workgroups go on to
+// stream rows).  When the rank units would take more than half of a
+// workgroup's share (short row runs would cut bands into many partial sums),
+// the rank workgroups take no rows at all ("separate" mode, S = Rw, D = 0)
+// and the rows are split over the other P - Rw.  Row parts
+// start on an even block of their band, so the bursts' code loads stay on
+// 128-byte lines; every workgroup from S on keeps at least one row unit.
+//
+// Arithmetic.  Unit counts stay below 2^21 (KB, NB <= 1024, RB <= 2) and the
+// cost axis below 2^22, so every product here (at most P <= 1024 times a
+// count) fits in 32 bits; the kernel calls these per band segment, and
+// 32-bit division is a fraction of 64-bit division's cost on the device.
+//
+// Partial sums.  A band covered by several workgroups is finished by the last
+// to arrive.  A workgroup's run meets at most two row bands that it does not
+// cover alone (the first and the last of its run), and the same for rank
+// bands, so its partial sums have fixed slots: row 2 w + {0: the band of its
+// first row unit, 1: any other}, rank 2 P + 2 w + {0, 1} likewise.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace spear {
+
+struct DecodeSplit {
+  int KB;       // 128-column blocks per row
+  int RB;       // rank bands (64 ranks each)
+  int NB;       // row bands
+  int P;        // workgroups
+  int Rw;       // workgroups [0, Rw) take rank units (0 when RB == 0)
+  int S;        // workgroups [0, S) take no row units: 0 (shared) or Rw (separate)
+  int D;        // row-unit equivalents a rank workgroup's rank units stand for (shared)
+  int C;        // the row cost axis: WU + (Rw - S) D
+};
+
+__host__ __device__ inline uint32_t split_ru(const DecodeSplit& d) {
+  return (uint32_t)d.RB * (uint32_t)d.KB;
+}
+__host__ __device__ inline uint32_t split_wu(const DecodeSplit& d) {
+  return (uint32_t)d.NB * (uint32_t)d.KB;
+}
+
+// First rank unit of workgroup w (RU for w >= Rw).
+__host__ __device__ inline uint32_t rank_begin(const DecodeSplit& d, int w) {
+  const uint32_t RU = split_ru(d);
+  return w >= d.Rw ? RU : (uint32_t)w * RU / (uint32_t)d.Rw;
+}
+// Workgroup whose rank run holds rank unit u (0 <= u < RU): the largest w
+// with rank_begin(w) <= u, i.e. ceil((u + 1) Rw / RU) - 1.
+__host__ __device__ inline int rank_owner(const DecodeSplit& d, uint32_t u) {
+  const uint32_t RU = split_ru(d);
+  return (int)(((u + 1) * (uint32_t)d.Rw + RU - 1) / RU) - 1;
+}
+
+// First row unit of workgroup w on the cost axis, before alignment.
+__host__ __device__ inline uint32_t row_begin_raw(const DecodeSplit& d, int w) {
+  const uint32_t wp = w > d.S ? (uint32_t)(w - d.S) : 0u;
+  const uint32_t Pp = (uint32_t)(d.P - d.S);
+  const uint32_t Rp = (uint32_t)(d.Rw - d.S);
+  return (wp * (uint32_t)d.C + Pp - 1) / Pp - (wp < Rp ? wp : Rp) * (uint32_t)d.D;
+}
+// First row unit of workgroup w (WU for w == P), moved to an even block.
+__host__ __device__ inline uint32_t row_begin(const DecodeSplit& d, int w) {
+  uint32_t b = row_begin_raw(d, w);
+  if (b > 0 && b < split_wu(d) && (b % (uint32_t)d.KB) % 2 == 1) ++b;
+  return b;
+}
+// Workgroup whose row run holds row unit u: the largest w with
+// row_begin(w) <= u (runs from S on are never empty).
+__host__ __device__ inline int row_owner(const DecodeSplit& d, uint32_t u) {
+  int lo = d.S, hi = d.P - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (row_begin(d, mid) <= u) lo = mid;
+    else hi = mid - 1;
+  }
+  return lo;
+}
+
+// Partial-sum slot of workgroup w for row band `band` / rank band `rb`.
+__host__ __device__ inline int row_slot(const DecodeSplit& d, int w, int band) {
+  return 2 * w + (row_begin(d, w) / (uint32_t)d.KB == (uint32_t)band ? 0 : 1);
+}
+__host__ __device__ inline int rank_slot(const DecodeSplit& d, int w, int rb) {
+  return 2 * d.P + 2 * w + (rank_begin(d, w) / (uint32_t)d.KB == (uint32_t)rb ? 0 : 1);
+}
+__host__ __device__ inline int split_slots(const DecodeSplit& d) { return 4 * d.P; }
+
+// The planner's constants: rank units per rank workgroup (four bursts; the
+// last arriver of a rank band sums one partial per rank workgroup), and what
+// a rank workgroup's share of the projection stands for in row units: 2.5
+// per rank unit (16 KB of A against 8 KB of codes, plus x) and a fixed 4 for
+// its hand-off of the partial projection.
+constexpr int kRankUnitsPerWg = 8;
+constexpr int kRankUnitCost2 = 5;   // twice the row-unit equivalents of one rank unit
+constexpr int kRankFixedCost = 4;
+
+// The split for P_max = slots workgroups.  Host only.
+inline DecodeSplit make_split(int KB, int RB, int NB, int slots) {
+  DecodeSplit d;
+  d.KB = KB;
+  d.RB = RB;
+  d.NB = NB;
+  const long long RU = (long long)RB * KB, WU = (long long)NB * KB;
+  slots = slots < 1 ? 1 : slots;
+  const long long prow = WU / 2 > 0 ? WU / 2 : 1;  // at least two row units per row workgroup
+  if (RU == 0) {
+    d.Rw = d.S = d.D = 0;
+    d.P = (int)(slots < prow ? slots : prow);
+    d.C = (int)WU;
+    return d;
+  }
+  long long Rw = (RU + kRankUnitsPerWg - 1) / kRankUnitsPerWg;
+  if (Rw > slots) Rw = slots;
+  const long long upw = (RU + Rw - 1) / Rw;
+  const long long D = (kRankUnitCost2 * upw + 1) / 2 + kRankFixedCost;
+  // shared: floor(C / P) >= 2 D + 2, so a rank workgroup keeps at least as
+  // many row units as its rank units stand for (and two at least)
+  long long p_sh = (WU + Rw * D) / (2 * D + 2);
+  if (p_sh > slots) p_sh = slots;
+  // separate: Rw rank workgroups, then P - Rw >= 1 row workgroups of >= 2
+  // units each (fewer rank workgroups if the slots run out)
+  if (Rw > slots - 1) Rw = slots - 1;
+  long long p_sep = Rw + prow;
+  if (p_sep > slots) p_sep = slots;
+  const long long rw_sh = (RU + kRankUnitsPerWg - 1) / kRankUnitsPerWg < slots
+                              ? (RU + kRankUnitsPerWg - 1) / kRankUnitsPerWg
+                              : slots;
+  if (p_sh >= rw_sh && (Rw < 1 || p_sh >= p_sep)) {
+    d.S = 0;
+    d.P = (int)p_sh;
+    d.D = (int)D;
+    d.Rw = (int)rw_sh;
+    d.C = (int)(WU + rw_sh * D);
+  } else if (Rw >= 1) {
+    d.S = (int)Rw;
+    d.Rw = (int)Rw;
+    d.P = (int)p_sep;
+    d.D = 0;
+    d.C = (int)WU;
+  } else {  // one workgroup takes everything
+    d.S = 0;
+    d.P = 1;
+    d.Rw = 1;
+    d.D = 0;
+    d.C = (int)WU;
+  }
+  return d;
+}
+
+// Partial-sum slots a workspace holds for a layer: enough for the split at
+// any slot count up to max_slots (P and Rw only shrink with fewer slots): two
+// per workgroup of the largest split, two per rank workgroup at most.  Host.
+inline int split_workspace_slots(int KB, int RB, int NB, int max_slots) {
+  const DecodeSplit big = make_split(KB, RB, NB, max_slots);
+  const long long RU = (long long)RB * KB;
+  long long rw = (RU + kRankUnitsPerWg - 1) / kRankUnitsPerWg;
+  if (rw > max_slots) rw = max_slots;
+  if (rw < big.Rw) rw = big.Rw;
+  return 2 * big.P + 2 * (int)rw;
+}
+
+}  // namespace spear

@@ -154,3 +154,25 @@ def test_quantize_and_dequant_validation(lib):
         binding.SPEAR_EC_ERR_MISALIGNED
     assert lib.spear_ec_dequant_f32(ctypes.byref(q.make_desc(256, 64, 0, 64, False)), 0x10000,
                                     0x20000, None, 0x30000, None) == binding.SPEAR_EC_ERR_UNSUPPORTED
+
+
+def test_workspace_status_validation(lib):
+    bits = ctypes.c_int32(-7)
+    assert lib.spear_ec_workspace_status(None, 1 << 20, None, ctypes.byref(bits)) == \
+        binding.SPEAR_EC_ERR_INVALID_ARGUMENT
+    assert lib.spear_ec_workspace_status(0x10000, 1 << 20, None, None) == \
+        binding.SPEAR_EC_ERR_INVALID_ARGUMENT
+    assert lib.spear_ec_workspace_status(0x10000, 8, None, ctypes.byref(bits)) == \
+        binding.SPEAR_EC_ERR_WORKSPACE
+    assert bits.value == -7          # nothing written on a validation error
+
+
+@pytest.mark.parametrize("name", ["spear_ec_linear", "spear_ec_linear_decode", "spear_ec_linear_prefill"])
+def test_output_flag_is_accepted_and_unknown_flags_are_not(lib, name):
+    f32 = q.make_desc(512, 512, 16, 512, False, out_f32=True)
+    assert f32.flags == binding.SPEAR_EC_OUT_F32
+    assert _call(lib, name, f32, 0) == binding.SPEAR_EC_OK
+    assert _call(lib, name, f32, 4, FAKE, ws_bytes=64) == binding.SPEAR_EC_ERR_WORKSPACE
+    bad = q.make_desc(512, 512, 16, 512, False)
+    bad.flags = 8
+    assert _call(lib, name, bad, 4, FAKE) == binding.SPEAR_EC_ERR_INVALID_ARGUMENT

@@ -2,15 +2,25 @@
 
 Each workload's layer is built at its real shape, quantized by both sides
 (bytes compared whole), and run through the dispatcher entry point exactly as
-bench.py calls it (one workspace sized for the call's token count).  The fp64
-oracle is too slow for every output of these layers, so it computes a sample
-of outputs one by one: the first and last token, the first and last rows,
-rows on both sides of the 128-row band edges (decode bands; every other one
-is a 256-row prefill tile edge) that the sample draws, and
-random (token, row) pairs.  The sampled outputs meet the same elementwise bar
-as the small cases; every output must be finite.
+bench.py calls it.  The fp64 oracle is evaluated on host threads over slices
+of output rows (its C functions release the interpreter lock), and compared:
+
+* decode calls (T <= 32): every output, all tokens x all rows;
+* prefill calls: every row of the chosen tokens, which are the first and
+  last token of every 128-token tile plus random ones, so every 128 x 256
+  output tile of the prefill kernel (and with it every split of K, each of
+  which adds into every output of its tile) is checked on 512 outputs at
+  least.  A token's outputs do not depend on the rest of its batch (a pinned
+  property of the oracle), so the oracle runs on those tokens alone.
+
+The bar is the elementwise one of the small cases (half a bf16 ulp + 2e-3 of
+max|y_ref|); with the fp32-output flag it is max|y - y_ref| / max|y_ref| <=
+2e-3 as stated, with no rounding allowance.  Every output must be finite and
+the workspace error word zero.
 """
 from __future__ import annotations
+
+import concurrent.futures as cf
 
 import numpy as np
 import pytest
@@ -18,10 +28,13 @@ import pytest
 import oracle
 import quantization_error_compensation_amd as q
 import synth
-from helpers import (REL_TOL, bf16_bits_to_f64, from_dev_u16, from_dev_u32, half_ulp_bf16,
+from helpers import (REL_TOL, bf16_bits_to_f64, check_bf16_output, from_dev_u16, from_dev_u32,
                      to_dev_bf16, to_dev_f32)
 
 pytestmark = pytest.mark.gpu
+
+THREADS = 8
+PREFILL_TILE = 128   # tokens per prefill output tile
 
 
 def note(msg):
@@ -36,32 +49,65 @@ def torch():
     return _t
 
 
-def sample_points(T, N, n_random, seed):
+def oracle_rows(x, wq, sc, zs, A, B, g, b, alpha, gs, mlp=None):
+    """oracle.forward over all rows, in row slices on host threads (the MLP
+    gate is a global setting of the oracle: one thread then)."""
+    N = wq.shape[0]
+    if mlp is not None:
+        return oracle.forward(x, wq, sc, zs, A, B, g, b, alpha, gs, mlp=mlp)
+    cuts = np.linspace(0, N // 16, THREADS + 1).astype(int) * 16
+    cuts[-1] = N
+
+    def part(i):
+        lo, hi = cuts[i], cuts[i + 1]
+        return oracle.forward(x, wq[lo:hi], sc[lo:hi], None if zs is None else zs[lo:hi], A,
+                              None if B is None else B[lo:hi], g, b, alpha, gs)
+    with cf.ThreadPoolExecutor(THREADS) as ex:
+        parts = list(ex.map(part, range(THREADS)))
+    return np.concatenate(parts, axis=1)
+
+
+def oracle_serq_rows(x, wq, sc, zs, s0, R, gs):
+    N = wq.shape[0]
+    cuts = np.linspace(0, N // 16, THREADS + 1).astype(int) * 16
+    cuts[-1] = N
+
+    def part(i):
+        lo, hi = cuts[i], cuts[i + 1]
+        return oracle.forward_serq(x, wq[lo:hi], sc[lo:hi], None if zs is None else zs[lo:hi], s0,
+                                   R[lo:hi], gs)
+    with cf.ThreadPoolExecutor(THREADS) as ex:
+        parts = list(ex.map(part, range(THREADS)))
+    return np.concatenate(parts, axis=1)
+
+
+def checked_tokens(T, seed):
+    """All tokens of a decode call; for prefill the first and last token of
+    every 128-token tile and four random ones."""
+    if T <= q.SPEAR_EC_DECODE_MAX_TOKENS:
+        return np.arange(T)
     rng = np.random.default_rng(seed)
-    ts = [0, T - 1] + list(rng.integers(0, T, n_random))
-    ns = [0, N - 1] + list(rng.integers(0, N, n_random))
-    edges = rng.integers(1, max(2, N // 128), 4) * 128        # band edges: rows 128k - 1, 128k
-    for e in edges:
-        if e < N:
-            ts += [int(rng.integers(0, T)), int(rng.integers(0, T))]
-            ns += [int(e) - 1, int(e)]
-    ts += [T - 1, 0]
-    ns += [0, N - 1]
-    return np.array(ts, np.int32), np.array(ns, np.int32)
+    ts = set()
+    for m0 in range(0, T, PREFILL_TILE):
+        ts.update((m0, min(T, m0 + PREFILL_TILE) - 1))
+    ts.update(int(t) for t in rng.integers(0, T, 4))
+    return np.array(sorted(ts))
 
 
-def check_sampled(y_bits, t_idx, n_idx, yref):
-    y = bf16_bits_to_f64(y_bits[t_idx, n_idx])
-    m = float(np.abs(yref).max())
-    err = np.abs(y - yref)
-    bound = half_ulp_bf16(yref) + REL_TOL * m
-    worst = int(np.argmax(err - bound))
-    return bool(np.all(err <= bound)), {"max_abs_err": float(err.max()), "ref_max": m,
-                                        "worst": (int(t_idx[worst]), int(n_idx[worst]))}
+def check(y_dev, y_ref, ts, f32):
+    if f32:
+        y = y_dev.cpu().numpy().astype(np.float64)[ts]
+        ratio = float(np.abs(y - y_ref).max() / np.abs(y_ref).max())
+        return ratio <= REL_TOL and bool(np.all(np.isfinite(y))), {"literal_ratio": ratio}
+    yb = from_dev_u16(y_dev)
+    ok, st = check_bf16_output(yb[ts], y_ref)
+    finite = bool(np.all(np.isfinite(bf16_bits_to_f64(yb))))
+    return ok and finite, dict(st, finite=finite)
 
 
 class FullLayer:
     def __init__(self, torch, name):
+        self.name = name
         self.spec = spec = synth.CONFIGS[name]
         self.K, self.N, self.g, self.asym = spec.d_in, spec.d_out, spec.group_size, spec.asym
         note(f"{name}: weights {self.N}x{self.K}, g={self.g}, asym={self.asym}")
@@ -85,38 +131,76 @@ class FullLayer:
             ok &= np.array_equal(from_dev_u32(self.d_zs), self.o_zs)
         return bool(ok)
 
-    def run_and_check(self, torch, T, r, seed):
+    def run_and_check(self, torch, T, r, seed, alpha=None, f32=False):
         spec = self.spec
+        alpha = spec.alpha if alpha is None else alpha
         x = synth.activations(spec, T)
         A, B, gv, bv = synth.compensator(spec, r)
-        desc = q.make_desc(self.K, self.N, r, self.g, self.asym, spec.per_tensor)
-        y = torch.empty((T, self.N), dtype=torch.bfloat16, device="cuda")
+        desc = q.make_desc(self.K, self.N, r, self.g, self.asym, spec.per_tensor, out_f32=f32)
+        y = torch.empty((T, self.N), dtype=torch.float32 if f32 else torch.bfloat16, device="cuda")
         ws = q.alloc_workspace(desc, T)
         dev = (to_dev_bf16(A), to_dev_bf16(B), to_dev_f32(gv), to_dev_f32(bv)) if r else (None,) * 4
-        note(f"  T={T} r={r}: spear_ec_linear")
-        q.spear_ec_linear(desc, to_dev_bf16(x), self.d_wq, self.d_sc, self.d_zs, *dev, spec.alpha,
-                          y, ws)
-        torch.cuda.synchronize()
-        err_word = int(ws[:16].view(torch.int32)[3].item())
-        yb = from_dev_u16(y)
-        ti, ni = sample_points(T, self.N, 200, seed)
-        yref = oracle.forward_sampled(x, self.o_wq, self.o_sc, self.o_zs, A if r else None, B, gv,
-                                      bv, spec.alpha, self.g, ti, ni)
-        ok, st = check_sampled(yb, ti, ni, yref)
-        finite = bool(np.all(np.isfinite(bf16_bits_to_f64(yb))))
-        return ok and finite and err_word == 0, dict(st, finite=finite, err_word=err_word)
+        note(f"  {self.name} T={T} r={r} alpha={alpha} f32={f32}: spear_ec_linear")
+        q.spear_ec_linear(desc, to_dev_bf16(x), self.d_wq, self.d_sc, self.d_zs, *dev, alpha, y, ws)
+        err = q.spear_ec_workspace_status(ws)
+        ts = checked_tokens(T, seed)
+        y_ref = oracle_rows(x[ts], self.o_wq, self.o_sc, self.o_zs, A if r else None,
+                            B if r else None, gv, bv, alpha, self.g)
+        ok, st = check(y, y_ref, ts, f32)
+        return ok and err == 0, dict(st, err_word=err, tokens_checked=int(len(ts)))
+
+
+@pytest.mark.parametrize("name,runs", [
+    ("c1", [(1, 32), (8, 32), (32, 32)]),
+    ("c2", [(2048, 64), (1, 64)]),
+    ("c3", [(16, 64), (512, 64), (1, 64), (32, 64)]),
+    ("c4", [(T, r) for T in (1, 16, 256, 4096) for r in synth.C4_RANKS]),
+    ("v1", [(9, 0), (2, 0), (5, 0)]),
+])
+def test_full_size_layer(torch, name, runs):
+    L = FullLayer(torch, name)
+    assert L.bytes_match(), f"{name}: quantized bytes differ"
+    for i, (T, r) in enumerate(runs):
+        ok, st = L.run_and_check(torch, T, r, seed=100 * i + T)
+        note(f"    {st}")
+        assert ok, (name, T, r, st)
+
+
+@pytest.mark.parametrize("name,runs", [
+    ("c1", [(8, 32, -0.75), (32, 32, 2.5)]),
+    ("c3", [(16, 64, 0.6), (512, 64, -1.3)]),
+])
+def test_full_size_alpha_other_than_one(torch, name, runs):
+    L = FullLayer(torch, name)
+    for i, (T, r, alpha) in enumerate(runs):
+        ok, st = L.run_and_check(torch, T, r, seed=300 + i, alpha=alpha)
+        note(f"    {st}")
+        assert ok, (name, T, r, alpha, st)
+
+
+@pytest.mark.parametrize("name,runs", [
+    ("c1", [(1, 32), (32, 32)]),
+    ("c2", [(2048, 64)]),
+    ("c3", [(16, 64), (512, 64)]),
+])
+def test_full_size_fp32_output_meets_the_literal_tolerance(torch, name, runs):
+    L = FullLayer(torch, name)
+    for i, (T, r) in enumerate(runs):
+        ok, st = L.run_and_check(torch, T, r, seed=500 + i, f32=True)
+        note(f"    {st}")
+        assert ok, (name, T, r, st)
 
 
 def test_full_size_mlp_gate_c3(torch):
     """The 70B down-projection with the bottleneck-MLP gate (h = 16): decode
-    (T = 16, 1) and prefill (T = 512), sampled against the oracle."""
+    (T = 16, 1) and prefill (T = 512) against the oracle."""
     L = FullLayer(torch, "c3")
     spec = L.spec
     m = synth.mlp_gate(spec, spec.rank, 16)
     dm = {k: to_dev_f32(v) for k, v in m.items()}
+    A, B, _, _ = synth.compensator(spec)
     for i, T in enumerate((16, 1, 512)):
         x = synth.activations(spec, T)
-        A, B, _, _ = synth.compensator(spec)
         desc = q.make_desc(L.K, L.N, spec.rank, L.g, L.asym)
         y = torch.empty((T, L.N), dtype=torch.bfloat16, device="cuda")
         ws = q.alloc_workspace(desc, T)
@@ -124,20 +208,17 @@ def test_full_size_mlp_gate_c3(torch):
         q.spear_ec_linear_mlp_gate(desc, to_dev_bf16(x), L.d_wq, L.d_sc, L.d_zs, to_dev_bf16(A),
                                    to_dev_bf16(B), dm["w1"], dm["b1"], dm["w2"], dm["b2"],
                                    spec.alpha, y, ws)
-        torch.cuda.synchronize()
-        assert int(ws[:16].view(torch.int32)[3].item()) == 0
-        ti, ni = sample_points(T, L.N, 200, 700 + i)
-        yref = oracle.forward_sampled(x, L.o_wq, L.o_sc, L.o_zs, A, B, None, None, spec.alpha,
-                                      L.g, ti, ni, mlp=m)
-        ok, st = check_sampled(from_dev_u16(y), ti, ni, yref)
+        assert q.spear_ec_workspace_status(ws) == 0
+        ts = checked_tokens(T, 700 + i)
+        y_ref = oracle_rows(x[ts], L.o_wq, L.o_sc, L.o_zs, A, B, None, None, spec.alpha, L.g, mlp=m)
+        ok, st = check(y, y_ref, ts, False)
         assert ok, (T, st)
 
 
 def test_full_size_serq_c3(torch):
     """The 70B down-projection with SERQ's single-matrix reconstruction of 64
     salient channels (at the front after the offline permutation, and at an
-    inner offset): decode (T = 16, 1, 32) and prefill (T = 512), sampled
-    against the oracle."""
+    inner offset): decode (T = 16, 1, 32) and prefill (T = 512)."""
     L = FullLayer(torch, "c3")
     spec = L.spec
     k = 64
@@ -150,24 +231,8 @@ def test_full_size_serq_c3(torch):
         ws = q.alloc_workspace(desc, T)
         note(f"  SERQ T={T} s0={s0}")
         q.spear_ec_linear_serq(desc, to_dev_bf16(x), L.d_wq, L.d_sc, L.d_zs, s0, dR, y, ws)
-        torch.cuda.synchronize()
-        assert int(ws[:16].view(torch.int32)[3].item()) == 0
-        ti, ni = sample_points(T, L.N, 200, 800 + i)
-        yref = oracle.forward_serq_sampled(x, L.o_wq, L.o_sc, L.o_zs, s0, R, L.g, ti, ni)
-        ok, st = check_sampled(from_dev_u16(y), ti, ni, yref)
+        assert q.spear_ec_workspace_status(ws) == 0
+        ts = checked_tokens(T, 800 + i)
+        y_ref = oracle_serq_rows(x[ts], L.o_wq, L.o_sc, L.o_zs, s0, R, L.g)
+        ok, st = check(y, y_ref, ts, False)
         assert ok, (T, s0, st)
-
-
-@pytest.mark.parametrize("name,runs", [
-    ("c1", [(1, 32), (8, 32), (32, 32)]),
-    ("c2", [(2048, 64), (1, 64)]),
-    ("c3", [(16, 64), (512, 64), (1, 64), (32, 64)]),
-    ("c4", [(1, 0), (1, 16), (1, 64), (1, 128), (16, 0), (16, 128), (256, 64), (4096, 128)]),
-    ("v1", [(9, 0), (2, 0), (5, 0)]),
-])
-def test_full_size_layer(torch, name, runs):
-    L = FullLayer(torch, name)
-    assert L.bytes_match(), f"{name}: quantized bytes differ"
-    for i, (T, r) in enumerate(runs):
-        ok, st = L.run_and_check(torch, T, r, seed=100 * i + T)
-        assert ok, (name, T, r, st)

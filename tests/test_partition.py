@@ -1,0 +1,83 @@
+"""The decode kernel's work split checked on the CPU (no GPU).
+
+tests/partition_check.cpp compiles the kernel's own partition header
+(quantization_error_compensation_amd/csrc/partition.hpp) for the host and
+checks it by brute force over a grid of layer shapes and workgroup counts:
+every rank and row unit has one owner and the owner functions the kernel
+uses find it, runs are non-empty and ordered, row runs start on an even
+block, each band's segment count (what the last-arriver count relies on)
+equals the number of workgroups that really meet it, and the partial-sum
+slots of shared bands are distinct and inside the workspace.
+"""
+import ctypes
+import os
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+SRC = os.path.join(ROOT, "tests", "partition_check.cpp")
+CSRC = os.path.join(ROOT, "quantization_error_compensation_amd", "csrc")
+OUT = os.path.join(ROOT, "tests", "_build", "libpartition_check.so")
+MAX_SLOTS = 256   # kMaxSlots of the library (one workgroup per compute unit)
+
+
+@pytest.fixture(scope="module")
+def lib():
+    os.makedirs(os.path.dirname(OUT), exist_ok=True)
+    extra = os.environ.get("SPEAR_SANITIZE_CXXFLAGS", "").split()   # set by the sanitizer test
+    out = OUT.replace(".so", "_san.so") if extra else OUT
+    subprocess.check_call(["g++", "-std=c++17", "-O2", "-shared", "-fPIC", "-D__HIP_PLATFORM_AMD__",
+                           *extra, "-I/opt/rocm/include", "-I", CSRC, SRC, "-o", out])
+    L = ctypes.CDLL(out)
+    L.check_split.argtypes = [ctypes.c_int] * 5 + [ctypes.POINTER(ctypes.c_longlong)]
+    L.check_split.restype = ctypes.c_int
+    L.check_message.restype = ctypes.c_char_p
+    return L
+
+
+def run(lib, K, N, r, slots):
+    KB, NB, RB = K // 128, (N + 127) // 128, (r + 63) // 64
+    st = (ctypes.c_longlong * 8)()
+    rc = lib.check_split(KB, RB, NB, slots, MAX_SLOTS, st)
+    assert rc == 0, (K, N, r, slots, lib.check_message().decode())
+    return dict(zip(("P", "Rw", "S", "D", "seg_row", "seg_rank", "ws_slots", "maxrun"), list(st)))
+
+
+LAYERS = [(128, 16), (128, 128), (256, 16), (512, 512), (1024, 48), (4096, 4096), (8192, 8192),
+          (4096, 11008), (28672, 8192), (2048, 1008), (131072, 128), (1152, 6400)]
+
+
+@pytest.mark.parametrize("K,N", LAYERS)
+@pytest.mark.parametrize("r", [0, 16, 64, 128])
+def test_split_holds_for_every_slot_count(lib, K, N, r):
+    for slots in (1, 2, 3, 7, 32, 100, 255, 256):
+        run(lib, K, N, r, slots)
+
+
+def test_large_layers(lib):
+    for K, N, r in ((131072, 131072, 128), (131072, 4096, 64), (16384, 131072, 16)):
+        run(lib, K, N, r, 256)
+
+
+@pytest.mark.parametrize("K,N,r", [(28672, 8192, 64), (8192, 8192, 128), (8192, 8192, 16),
+                                   (8192, 8192, 64)])
+def test_benchmark_layers_fill_the_device(lib, K, N, r):
+    # at full size every compute unit gets a workgroup and a rank band is
+    # shared by a bounded number of rank workgroups
+    st = run(lib, K, N, r, 256)
+    assert st["P"] == 256 and 8 <= st["Rw"] <= 32 and st["seg_rank"] <= 32, st
+
+
+def test_the_70b_layer_shares_rank_workgroups_with_rows(lib):
+    # 28672 -> 8192: a rank workgroup's eight rank units are a small part of
+    # its share, so it goes on to stream rows (shared mode)
+    st = run(lib, 28672, 8192, 64, 256)
+    assert st["S"] == 0 and st["D"] > 0, st
+
+
+def test_small_layers_keep_rank_workgroups_apart(lib):
+    # a 4096 x 4096 layer is too small for a rank workgroup to also take two
+    # row units: its rank workgroups take no rows and the rows go to the rest
+    st = run(lib, 4096, 4096, 32, 256)
+    assert st["S"] == st["Rw"] >= 1 and st["P"] == 256, st
