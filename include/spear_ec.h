@@ -141,6 +141,26 @@ int spear_ec_linear(const spear_ec_desc* desc, int32_t tokens, const void* x,
                     hipStream_t stream);
 
 /*
+ * spear_ec_linear without a workspace argument, for callers that cannot
+ * allocate memory (code under stream capture into a HIP graph, tight serving
+ * loops, harnesses that forbid hipMalloc): the call runs on the library's own
+ * scratch, a file-scope device array of 64 MiB on each device the library
+ * runs on (held until the process ends; its address is looked up and its
+ * counters cleared on the device's first call).  It allocates nothing and
+ * calls no allocating routine.  All calls on one device share that scratch:
+ * calls that overlap on a device (several streams or threads at once) race.
+ * The decode kernel's error word lives in that scratch and is not reported
+ * (an output that a failed wait could not finish still holds NaN).  Same
+ * arguments, dispatch and status codes as spear_ec_linear otherwise; a call
+ * that needs more than 64 MiB of scratch (spear_ec_workspace_bytes of its
+ * shape and token count) returns SPEAR_EC_ERR_WORKSPACE, before any HIP call.
+ */
+int spear_ec_linear_static(const spear_ec_desc* desc, int32_t tokens, const void* x,
+                           const uint32_t* wq, const void* scales, const uint32_t* zeros,
+                           const void* A, const void* B, const float* g, const float* b,
+                           float alpha, void* y, hipStream_t stream);
+
+/*
  * Decode path, 1..32 tokens (memory-bound: streams the packed weights once;
  * the rank-r projection is computed once per token and the gated B term is
  * added in registers before the single store of y).  tokens > 32 returns

@@ -13,6 +13,7 @@ from .binding import (  # noqa: F401
     load_library, make_desc,
     spear_ec_dequant_f32, spear_ec_desc, spear_ec_last_error, spear_ec_linear,
     spear_ec_linear_decode, spear_ec_linear_mlp_gate, spear_ec_linear_prefill,
+    spear_ec_linear_static,
     spear_ec_linear_serq, spear_ec_lut_kind, spear_ec_lut_measure, spear_ec_pick_chunk,
     spear_ec_step_latency_us,
     spear_ec_quantize_rtn,

@@ -31,7 +31,8 @@ SPEAR_EC_DECODE_MAX_TOKENS = 32
 
 EXPORTED = (
     "spear_ec_workspace_bytes", "spear_ec_workspace_status", "spear_ec_linear", "spear_ec_linear_decode",
-    "spear_ec_linear_prefill", "spear_ec_linear_mlp_gate", "spear_ec_linear_serq",
+    "spear_ec_linear_prefill", "spear_ec_linear_static", "spear_ec_linear_mlp_gate",
+    "spear_ec_linear_serq",
     "spear_ec_step_latency_us", "spear_ec_pick_chunk", "spear_ec_lut_measure",
     "spear_ec_quantize_rtn",
     "spear_ec_dequant_f32", "spear_ec_status_string", "spear_ec_last_error", "spear_ec_version",
@@ -76,6 +77,8 @@ def load_library(path: str = LIB_PATH):
     for name in ("spear_ec_linear", "spear_ec_linear_decode", "spear_ec_linear_prefill"):
         getattr(lib, name).argtypes = lin
         getattr(lib, name).restype = ctypes.c_int
+    lib.spear_ec_linear_static.argtypes = [DP, i32, P, P, P, P, P, P, P, P, ctypes.c_float, P, P]
+    lib.spear_ec_linear_static.restype = ctypes.c_int
     lib.spear_ec_linear_mlp_gate.argtypes = [DP, i32, P, P, P, P, P, P, i32, P, P, P, P,
                                              ctypes.c_float, P, P, sz, P]
     lib.spear_ec_linear_mlp_gate.restype = ctypes.c_int
@@ -185,6 +188,13 @@ def spear_ec_linear_prefill(desc, x, wq, scales, zeros, A, B, g, b, alpha, y, wo
                             stream=None):
     _linear("spear_ec_linear_prefill", desc, x, wq, scales, zeros, A, B, g, b, alpha, y,
             workspace, stream)
+
+
+def spear_ec_linear_static(desc, x, wq, scales, zeros, A, B, g, b, alpha, y, stream=None):
+    """spear_ec_linear on the library's own scratch (no workspace argument)."""
+    _check(load_library().spear_ec_linear_static(
+        ctypes.byref(desc), int(x.shape[0]), _ptr(x), _ptr(wq), _ptr(scales), _ptr(zeros), _ptr(A),
+        _ptr(B), _ptr(g), _ptr(b), float(alpha), _ptr(y), _stream(stream)))
 
 
 def spear_ec_linear_mlp_gate(desc, x, wq, scales, zeros, A, B, w1, b1, w2, b2, alpha, y,

@@ -19,7 +19,8 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(os.path.dirname(HERE), "include")
 LIB = os.path.join(HERE, "libspear_ec.so")
 BUILD_DIR = os.path.join(HERE, "_build")
-SOURCES = ["api.hip", "k_quant.hip", "k_proj.hip", "k_decode.hip", "k_prefill.hip", "scheduler.cpp"]
+SOURCES = ["api.hip", "static_scratch.hip", "k_quant.hip", "k_proj.hip", "k_decode.hip",
+           "k_prefill.hip", "scheduler.cpp"]
 ARCH = os.environ.get("SPEAR_EC_ARCH", "gfx950")
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

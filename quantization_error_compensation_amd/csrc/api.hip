@@ -164,11 +164,14 @@ struct MlpGate {
   const float *w1, *b1, *w2, *b2;
 };
 
+// use_static: the call runs on the library's own scratch (workspace and
+// workspace_bytes are ignored); it is looked up only after every check passed.
 static int linear(Path path, const spear_ec_desc* d, int32_t tokens, const void* x,
                   const uint32_t* wq, const void* scales, const uint32_t* zeros, const void* A,
                   const void* B, const float* g, const float* b, float alpha, void* y,
                   void* workspace, size_t workspace_bytes, hipStream_t stream,
-                  const MlpGate& mlp = MlpGate{0, nullptr, nullptr, nullptr, nullptr}) {
+                  const MlpGate& mlp = MlpGate{0, nullptr, nullptr, nullptr, nullptr},
+                  bool use_static = false) {
   g_last_error[0] = 0;
   int rc = check_desc(d, true);
   if (rc) return rc;
@@ -185,9 +188,9 @@ static int linear(Path path, const spear_ec_desc* d, int32_t tokens, const void*
     return fail(SPEAR_EC_ERR_INVALID_ARGUMENT, "A, B, g and b are required when rank > 0");
   if (gmlp && (!A || !B || !mlp.w1 || !mlp.b1 || !mlp.w2 || !mlp.b2))
     return fail(SPEAR_EC_ERR_INVALID_ARGUMENT, "A, B, w1, b1, w2 and b2 are required when rank > 0");
-  if (!workspace) return fail(SPEAR_EC_ERR_WORKSPACE, "workspace is NULL");
+  if (!use_static && !workspace) return fail(SPEAR_EC_ERR_WORKSPACE, "workspace is NULL");
   const bool eg = d->rank > 0 && !gmlp;
-  const void* ptrs[] = {x, wq, scales, y, workspace, has_z ? zeros : nullptr,
+  const void* ptrs[] = {x, wq, scales, y, use_static ? nullptr : workspace, has_z ? zeros : nullptr,
                         d->rank ? A : nullptr, d->rank ? B : nullptr, eg ? g : nullptr,
                         eg ? b : nullptr, gmlp ? mlp.w1 : nullptr, gmlp ? mlp.b1 : nullptr,
                         gmlp ? mlp.w2 : nullptr, gmlp ? mlp.b2 : nullptr};
@@ -196,7 +199,14 @@ static int linear(Path path, const spear_ec_desc* d, int32_t tokens, const void*
   const bool decode = path == kDecode || (path == kAuto && tokens <= SPEAR_EC_DECODE_MAX_TOKENS);
   const Shape s = make_shape(d, tokens);
   const Workspace wl = layout(s, decode);
-  if (workspace_bytes < wl.total) return fail(SPEAR_EC_ERR_WORKSPACE, "workspace is smaller than spear_ec_workspace_bytes()");
+  if (use_static) {
+    if (wl.total > kStaticScratchBytes)
+      return fail(SPEAR_EC_ERR_WORKSPACE, "the call needs more than the static scratch (64 MiB)");
+    rc = hip_status(static_scratch(&workspace, stream), "static scratch set-up");
+    if (rc) return rc;
+  } else if (workspace_bytes < wl.total) {
+    return fail(SPEAR_EC_ERR_WORKSPACE, "workspace is smaller than spear_ec_workspace_bytes()");
+  }
 
   LayerArgs a;
   a.x = x;
@@ -327,6 +337,14 @@ int spear_ec_linear(const spear_ec_desc* desc, int32_t tokens, const void* x, co
                     size_t workspace_bytes, hipStream_t stream) {
   return linear(kAuto, desc, tokens, x, wq, scales, zeros, A, B, g, b, alpha, y, workspace,
                 workspace_bytes, stream);
+}
+
+int spear_ec_linear_static(const spear_ec_desc* desc, int32_t tokens, const void* x,
+                           const uint32_t* wq, const void* scales, const uint32_t* zeros,
+                           const void* A, const void* B, const float* g, const float* b,
+                           float alpha, void* y, hipStream_t stream) {
+  return linear(kAuto, desc, tokens, x, wq, scales, zeros, A, B, g, b, alpha, y, nullptr, 0, stream,
+                MlpGate{0, nullptr, nullptr, nullptr, nullptr}, true);
 }
 
 int spear_ec_linear_decode(const spear_ec_desc* desc, int32_t tokens, const void* x,

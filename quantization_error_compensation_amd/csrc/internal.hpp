@@ -20,6 +20,7 @@ constexpr int kPrefillBN = 256;       // output rows per prefill tile
 constexpr int kPrefillWaves = 8;      // waves per prefill workgroup (2 x 4 of 64 x 64)
 constexpr int kPrefillTarget = 256;   // split K until a call has at least this many workgroups
 constexpr int kCounterSlots = 4096;   // int32 words at the head of the workspace
+constexpr size_t kStaticScratchBytes = (size_t)64 << 20;  // the library's own scratch per device
 
 // Decode counter words (all zero between calls).
 constexpr int kCtrRankDone = 1;  // rank bands whose gated projection is published
@@ -116,6 +117,9 @@ hipError_t launch_projection(const Shape& s, const LayerArgs& a, const WsPtrs& w
 hipError_t launch_decode(const Shape& s, const LayerArgs& a, const WsPtrs& w, hipStream_t st);
 hipError_t launch_prefill(const Shape& s, const LayerArgs& a, const WsPtrs& w, hipStream_t st);
 hipError_t launch_serq_operand(const Shape& s, const LayerArgs& a, const WsPtrs& w, hipStream_t st);
+// Device address of the library's static scratch on the current device
+// (looked up and its counter words cleared on the device's first use).
+hipError_t static_scratch(void** out, hipStream_t st);
 hipError_t launch_quantize(int N, int K, int g, bool asym, bool per_tensor, const float* w,
                            uint32_t* wq, uint16_t* scales, uint32_t* zeros, hipStream_t st);
 hipError_t launch_dequant(int N, int K, int g, const uint32_t* wq, const uint16_t* scales,

@@ -29,4 +29,5 @@ hipError_t launch_dequant(int, int, int, const uint32_t*, const uint16_t*, const
                           hipStream_t) {
   return hipErrorNotSupported;
 }
+hipError_t static_scratch(void**, hipStream_t) { return hipErrorNotSupported; }
 }  // namespace spear

@@ -176,3 +176,25 @@ def test_output_flag_is_accepted_and_unknown_flags_are_not(lib, name):
     bad = q.make_desc(512, 512, 16, 512, False)
     bad.flags = 8
     assert _call(lib, name, bad, 4, FAKE) == binding.SPEAR_EC_ERR_INVALID_ARGUMENT
+
+
+def _call_static(lib, desc, tokens, ptrs, alpha=1.0):
+    get = lambda k: ptrs.get(k)  # noqa: E731
+    return lib.spear_ec_linear_static(ctypes.byref(desc) if desc is not None else None, tokens,
+                                      get("x"), get("wq"), get("sc"), get("z"), get("A"), get("B"),
+                                      get("g"), get("b"), alpha, get("y"), None)
+
+
+def test_static_scratch_entry_validation(lib):
+    good = q.make_desc(512, 512, 16, 512, False)
+    assert _call_static(lib, None, 4, FAKE) == binding.SPEAR_EC_ERR_INVALID_ARGUMENT
+    assert _call_static(lib, good, -1, FAKE) == binding.SPEAR_EC_ERR_INVALID_ARGUMENT
+    assert _call_static(lib, good, 0, {}) == binding.SPEAR_EC_OK          # no-op
+    assert _call_static(lib, good, 4, {**FAKE, "y": None}) == binding.SPEAR_EC_ERR_INVALID_ARGUMENT
+    assert _call_static(lib, good, 4, {**FAKE, "A": FAKE["A"] + 2}) == binding.SPEAR_EC_ERR_MISALIGNED
+    assert _call_static(lib, q.make_desc(512, 520, 16, 512, False), 4, FAKE) == \
+        binding.SPEAR_EC_ERR_UNSUPPORTED
+    # more scratch than the library holds: rejected before any HIP call
+    big = q.make_desc(131072, 131072, 128, 128, True)
+    assert _call_static(lib, big, 65536, FAKE) == binding.SPEAR_EC_ERR_WORKSPACE
+    assert "static scratch" in q.spear_ec_last_error()
