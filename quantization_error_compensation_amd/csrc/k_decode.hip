@@ -40,11 +40,19 @@
 // The band finisher adds alpha * B * v as a small K = r matrix-core product
 // (v split into bf16 high and low parts) and stores y.
 //
-// Waiting: finishers of row bands wait for the rank bands to publish.  Rank
-// units belong to the lowest workgroup indices, which the dispatcher starts
-// first; a rank workgroup never waits before it has published its share, so
-// the waits end whenever those workgroups get compute units.  The wait is
-// bounded all the same: one that gives up writes NaN and sets an error bit
+// The projection.  Each rank workgroup stores its partial projection of a
+// rank band in its slot and posts it with an atomic whose result it does not
+// wait for, then goes on to its row units.  Workgroup 0, which takes no row
+// units, waits for every post of a band, sums the partials in workgroup
+// order, gates, publishes alpha * v and raises the count that the row
+// finishers wait for.  So the reduction delays no row stream.
+//
+// Waiting: row finishers wait for that count, and workgroup 0 for the posts.
+// Rank units belong to the lowest workgroup indices, which the dispatcher
+// starts first, and a rank workgroup posts before it waits for anything;
+// with one workgroup per compute unit and no more workgroups than compute
+// units every wait ends.  The waits are bounded all the same: one that gives
+// up writes NaN (or publishes NaN) and sets an error bit
 // (spear_ec_workspace_status).
 #include "common.hpp"
 #include "internal.hpp"
@@ -752,26 +760,84 @@ __device__ __forceinline__ void store_row(const DecodeParams& p, int band, const
       }
 }
 
-// Add this workgroup's partial sum of a band (shared by workgroups first ..
-// first + nseg - 1) and report whether it arrived last; the last one gets
-// the sum of all partials in workgroup order in v and clears the band's
-// counter (counter cband).  Waves with act false (those past the 64 columns
-// of a rank band) hold no column.
+// Add this workgroup's partial sum of row band `band` (shared by workgroups
+// first .. first + nseg - 1) and report whether it arrived last; the last one
+// gets the sum of all partials in workgroup order in v and clears the band's
+// counter.
 template <int MT>
-__device__ __forceinline__ bool arrive(const DecodeParams& p, bool rank, int band, int cband,
-                                       int first, int nseg, bool act, int* s_last, f32x4 (&v)[MT]) {
+__device__ __forceinline__ bool arrive(const DecodeParams& p, int band, int first, int nseg,
+                                       int* s_last, f32x4 (&v)[MT]) {
   const int tid = threadIdx.x, col = 16 * wave_id() + (tid & 15);
-  if (act) put_part<MT>(p, slot_of(p, rank, blockIdx.x, band), col, v);
+  int* ctr = &p.ctr[kCtrBand + p.RB + band];
+  put_part<MT>(p, slot_of(p, false, blockIdx.x, band), col, v);
   wait_vmem();
   __syncthreads();
-  if (tid == 0) *s_last = atomicAdd(&p.ctr[kCtrBand + cband], 1) == nseg - 1;
+  if (tid == 0) *s_last = atomicAdd(ctr, 1) == nseg - 1;
   __syncthreads();
   const bool last = *s_last;
   if (last) {
-    if (act) sum_parts<MT>(p, rank, band, first, nseg, col, v);
-    if (tid == 0) store_dev(&p.ctr[kCtrBand + cband], 0);
+    sum_parts<MT>(p, false, band, first, nseg, col, v);
+    if (tid == 0) store_dev(ctr, 0);
   }
   return last;
+}
+
+// A rank workgroup's partial projection of rank band rb: stored in its slot
+// (the 64 columns are in waves 0-3), then counted on the band's counter with
+// an atomic whose result is not awaited.
+template <int MT>
+__device__ __forceinline__ void post_rank_part(const DecodeParams& p, int rb, const f32x4 (&v)[MT]) {
+  const int tid = threadIdx.x, col = 16 * wave_id() + (tid & 15);
+  if (wave_id() < 4) put_part<MT>(p, slot_of(p, true, blockIdx.x, rb), col, v);
+  wait_vmem();
+  __syncthreads();
+  if (tid == 0)
+    __hip_atomic_fetch_add(&p.ctr[kCtrBand + rb], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Workgroup 0: for each rank band, wait (bounded) until all its rank
+// workgroups have posted, sum their partials in workgroup order, gate and
+// publish alpha v (the MLP gate: u, then the gate pass over all ranks), and
+// raise the count the row finishers wait for.  A wait that gives up
+// publishes NaN and sets the error word.
+template <int MT>
+__device__ void reduce_ranks(const DecodeParams& p, uint8_t* xlds, int* s_flag) {
+  const DecodeSplit& sp = p.sp;
+  const int tid = threadIdx.x, col = 16 * wave_id() + (tid & 15);
+  for (int rb = 0; rb < p.RB; ++rb) {
+    const uint32_t bbeg = (uint32_t)rb * p.KB;
+    const int first = rank_owner(sp, bbeg);
+    const int nseg = rank_owner(sp, bbeg + p.KB - 1) - first + 1;
+    int* ctr = &p.ctr[kCtrBand + rb];
+    if (tid == 0) {
+      int spins = 0, ok = 1;
+      while (load_dev(ctr) < nseg) {
+        __builtin_amdgcn_s_sleep(1);
+        if (++spins > kSpinLimit) {
+          atomicOr(&p.ctr[kCtrError], 1);
+          ok = 0;
+          break;
+        }
+      }
+      *s_flag = ok;
+    }
+    __syncthreads();
+    const bool ok = *s_flag != 0;
+    __syncthreads();
+    f32x4 v[MT];
+    if (wave_id() < 4) sum_parts<MT>(p, true, rb, first, nseg, col, v);
+    if (!ok)
+      for (int mt = 0; mt < MT; ++mt) v[mt] = f32x4{NAN, NAN, NAN, NAN};
+    if (tid == 0) store_dev(ctr, 0);
+    finish_rank<MT>(p, rb, v);
+  }
+  wait_vmem();
+  __syncthreads();
+  if (p.gh > 0) {
+    gate_mlp(p, xlds, 2 * Burst<MT>::kBuf / 4);
+  } else if (tid == 0) {
+    __hip_atomic_fetch_add(&p.ctr[kCtrRankDone], p.RB, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
 }
 
 // Second bound: waves per SIMD (one workgroup of W waves per compute unit),
@@ -789,56 +855,56 @@ __global__ __launch_bounds__(kThreads, W * kDecodeOccupancy / 4) void decode_ker
   const DecodeSplit& sp = p.sp;
   int burst = 0;
 
-  // Rank units first (workgroups below sp.Rw), then row units.
-  for (int pass = 0; pass < 2; ++pass) {
-    const bool rank = pass == 0;
-    const uint32_t u0 = rank ? rank_begin(sp, wg) : row_begin(sp, wg);
-    const uint32_t u1 = rank ? rank_begin(sp, wg + 1) : row_begin(sp, wg + 1);
-    for (uint32_t u = u0; u < u1;) {
-      const int band = (int)(u / (uint32_t)p.KB);  // rank band, or row band
+  // Rank runs (workgroups below sp.Rw): each partial projection goes to its
+  // slot and is posted without waiting for the count; workgroup 0 then sums
+  // every rank band, gates and publishes alpha v.
+  {
+    const uint32_t u1 = rank_begin(sp, wg + 1);
+    for (uint32_t u = rank_begin(sp, wg); u < u1;) {
+      const int band = (int)fdiv(u, sp.by_kb);
       const uint32_t bbeg = (uint32_t)band * p.KB, bend = bbeg + p.KB;
       const int lo = (int)(u - bbeg);
       const int hi = (int)(min(u1, bend) - bbeg);
       u = min(u1, bend);
-      const int first = rank ? rank_owner(sp, bbeg) : row_owner(sp, bbeg);
-      const int nseg = (rank ? rank_owner(sp, bend - 1) : row_owner(sp, bend - 1)) - first + 1;
-      const int cband = rank ? band : p.RB + band;  // arrival counter
-
       f32x4 v[MT];
-      if (rank) rank_segment<MT>(p, band, lo, hi, xlds, burst, v);
-      else row_segment<MT, GROUPED>(p, band, lo, hi, xlds, mlds, burst, v);
-
-      const bool fin = nseg == 1 || arrive<MT>(p, rank, band, cband, first, nseg,
-                                               !rank || wave_id() < 4, &s_last, v);
-      if (!fin) continue;
-      if (rank) {
-        finish_rank<MT>(p, band, v);
-        wait_vmem();
-        __syncthreads();
-        if (tid == 0) s_last = atomicAdd(&p.ctr[kCtrRankDone], 1) == p.RB - 1;
-        __syncthreads();
-        if (p.gh > 0 && s_last) gate_mlp(p, xlds, 2 * Burst<MT>::kBuf / 4);
-      } else {
-        if (p.r > 0) {
-          u32x4 bfr[kRankSteps];
-          b_fragments(p, band, bfr);
-          u32x4 vhi[kRankSteps][MT], vlo[kRankSteps][MT];
-          if (p.s0 >= 0) {  // SERQ: x's salient channels, nothing to wait for
-            serq_operands<MT>(p, vhi);
-            for (int k = 0; k < kRankSteps; ++k)
-              for (int mt = 0; mt < MT; ++mt) vlo[k][mt] = u32x4{0u, 0u, 0u, 0u};
-          } else if (wait_ranks(p, &s_wait)) {
-            alpha_v_operands<MT>(p, vhi, vlo);
-          } else {  // gave up waiting: no plausible-looking output
-            for (int mt = 0; mt < MT; ++mt) v[mt] = f32x4{NAN, NAN, NAN, NAN};
-            for (int k = 0; k < kRankSteps; ++k)
-              for (int mt = 0; mt < MT; ++mt) vhi[k][mt] = vlo[k][mt] = u32x4{0u, 0u, 0u, 0u};
-          }
-          add_correction<MT>(p, bfr, vhi, vlo, v);
-        }
-        store_row<MT>(p, band, v);
-      }
+      rank_segment<MT>(p, band, lo, hi, xlds, burst, v);
+      post_rank_part<MT>(p, band, v);
     }
+    if (wg == 0 && p.RB > 0) reduce_ranks<MT>(p, xlds, &s_wait);
+  }
+
+  // Row runs.
+  const uint32_t u1 = row_begin(sp, wg + 1);
+  for (uint32_t u = row_begin(sp, wg); u < u1;) {
+    const int band = (int)fdiv(u, sp.by_kb);
+    const uint32_t bbeg = (uint32_t)band * p.KB, bend = bbeg + p.KB;
+    const int lo = (int)(u - bbeg);
+    const int hi = (int)(min(u1, bend) - bbeg);
+    u = min(u1, bend);
+    const int first = row_owner(sp, bbeg);
+    const int nseg = row_owner(sp, bend - 1) - first + 1;
+
+    f32x4 v[MT];
+    row_segment<MT, GROUPED>(p, band, lo, hi, xlds, mlds, burst, v);
+    if (nseg > 1 && !arrive<MT>(p, band, first, nseg, &s_last, v)) continue;
+    if (p.r > 0) {
+      u32x4 bfr[kRankSteps];
+      b_fragments(p, band, bfr);
+      u32x4 vhi[kRankSteps][MT], vlo[kRankSteps][MT];
+      if (p.s0 >= 0) {  // SERQ: x's salient channels, nothing to wait for
+        serq_operands<MT>(p, vhi);
+        for (int k = 0; k < kRankSteps; ++k)
+          for (int mt = 0; mt < MT; ++mt) vlo[k][mt] = u32x4{0u, 0u, 0u, 0u};
+      } else if (wait_ranks(p, &s_wait)) {
+        alpha_v_operands<MT>(p, vhi, vlo);
+      } else {  // gave up waiting: no plausible-looking output
+        for (int mt = 0; mt < MT; ++mt) v[mt] = f32x4{NAN, NAN, NAN, NAN};
+        for (int k = 0; k < kRankSteps; ++k)
+          for (int mt = 0; mt < MT; ++mt) vhi[k][mt] = vlo[k][mt] = u32x4{0u, 0u, 0u, 0u};
+      }
+      add_correction<MT>(p, bfr, vhi, vlo, v);
+    }
+    store_row<MT>(p, band, v);
   }
 
   if (p.RB > 0 && tid == 0) {

@@ -9,23 +9,29 @@
 // Rank units.  Workgroups [0, Rw) take contiguous, near-equal runs of the
 // rank units, rank_begin(w) = floor(w RU / Rw), so the rank-r projection is
 // spread over many compute units and is published early (every row band's
-// finisher waits for it).
+// finisher waits for it).  Workgroup 0 sums the partial projections and
+// publishes the gated result; it takes no row units (unless it is the only
+// workgroup), so that work delays no row stream.
 //
 // Row units.  Laid out as a stream-K split over a cost axis of C row-unit
 // equivalents: workgroup w owns [w C / P', (w + 1) C / P') (P' = P - S, w
 // counted from S), and a rank workgroup spends the first D units of its
-// range on its rank units ("shared" mode, S = 0: rank workgroups go on to
-// stream rows).  When the rank units would take more than half of a
-// workgroup's share (short row runs would cut bands into many partial sums),
-// the rank workgroups take no rows at all ("separate" mode, S = Rw, D = 0)
-// and the rows are split over the other P - Rw.  Row parts
+// range on its rank units ("shared" mode, S = 1: the rank workgroups but the
+// first go on to stream rows).  When the rank units would take more than
+// half of a workgroup's share (short row runs would cut bands into many
+// partial sums), the rank workgroups take no rows at all ("separate" mode,
+// S = Rw, D = 0) and the rows are split over the other P - Rw.  Row parts
 // start on an even block of their band, so the bursts' code loads stay on
 // 128-byte lines; every workgroup from S on keeps at least one row unit.
 //
 // Arithmetic.  Unit counts stay below 2^21 (KB, NB <= 1024, RB <= 2) and the
-// cost axis below 2^22, so every product here (at most P <= 1024 times a
-// count) fits in 32 bits; the kernel calls these per band segment, and
-// 32-bit division is a fraction of 64-bit division's cost on the device.
+// cost axis below 2^22, so every numerator here (at most P <= 256 times a
+// count) is below 2^31.  The GPU has no integer divider: a division by a
+// value known only at run time is a dependent sequence of some thirty
+// instructions, and the owner searches take dozens of them before a
+// workgroup's first load.  Every divisor here is fixed per call, so the host
+// computes a multiplier for each (FastDiv) and a division becomes one
+// 32 x 32 -> 64-bit multiply and a shift.
 //
 // Partial sums.  A band covered by several workgroups is finished by the last
 // to arrive.  A workgroup's run meets at most two row bands that it does not
@@ -39,15 +45,40 @@
 
 namespace spear {
 
+// Division by a fixed d >= 1 for numerators n < 2^31 (the round-up method:
+// with l = ceil(log2 d), m = ceil(2^(31+l) / d) <= 2^31 and
+// floor(n m / 2^(31+l)) = floor(n / d) for every such n).
+struct FastDiv {
+  uint32_t d, m, s;
+};
+inline FastDiv make_fastdiv(uint32_t d) {
+  uint32_t l = 0;
+  while ((1ull << l) < d) ++l;
+  const unsigned long long two = 1ull << (31 + l);
+  FastDiv f;
+  f.d = d;
+  f.m = (uint32_t)((two + d - 1) / d);
+  f.s = 31 + l;
+  return f;
+}
+__host__ __device__ inline uint32_t fdiv(uint32_t n, const FastDiv& f) {
+  return (uint32_t)(((unsigned long long)n * f.m) >> f.s);
+}
+__host__ __device__ inline uint32_t fmod(uint32_t n, const FastDiv& f) {
+  return n - fdiv(n, f) * f.d;
+}
+
 struct DecodeSplit {
   int KB;       // 128-column blocks per row
   int RB;       // rank bands (64 ranks each)
   int NB;       // row bands
   int P;        // workgroups
   int Rw;       // workgroups [0, Rw) take rank units (0 when RB == 0)
-  int S;        // workgroups [0, S) take no row units: 0 (shared) or Rw (separate)
+  int S;        // workgroups [0, S) take no row units: 1 (shared), Rw (separate), 0 (no
+                // rank units, or one workgroup)
   int D;        // row-unit equivalents a rank workgroup's rank units stand for (shared)
-  int C;        // the row cost axis: WU + (Rw - S) D
+  int C;        // the row cost axis: WU + (Rw - S) D (shared mode)
+  FastDiv by_kb, by_pp, by_rw, by_ru;  // KB, P - S, Rw, RU (1 when zero)
 };
 
 __host__ __device__ inline uint32_t split_ru(const DecodeSplit& d) {
@@ -60,13 +91,13 @@ __host__ __device__ inline uint32_t split_wu(const DecodeSplit& d) {
 // First rank unit of workgroup w (RU for w >= Rw).
 __host__ __device__ inline uint32_t rank_begin(const DecodeSplit& d, int w) {
   const uint32_t RU = split_ru(d);
-  return w >= d.Rw ? RU : (uint32_t)w * RU / (uint32_t)d.Rw;
+  return w >= d.Rw ? RU : fdiv((uint32_t)w * RU, d.by_rw);
 }
 // Workgroup whose rank run holds rank unit u (0 <= u < RU): the largest w
 // with rank_begin(w) <= u, i.e. ceil((u + 1) Rw / RU) - 1.
 __host__ __device__ inline int rank_owner(const DecodeSplit& d, uint32_t u) {
   const uint32_t RU = split_ru(d);
-  return (int)(((u + 1) * (uint32_t)d.Rw + RU - 1) / RU) - 1;
+  return (int)fdiv((u + 1) * (uint32_t)d.Rw + RU - 1, d.by_ru) - 1;
 }
 
 // First row unit of workgroup w on the cost axis, before alignment.
@@ -74,12 +105,12 @@ __host__ __device__ inline uint32_t row_begin_raw(const DecodeSplit& d, int w) {
   const uint32_t wp = w > d.S ? (uint32_t)(w - d.S) : 0u;
   const uint32_t Pp = (uint32_t)(d.P - d.S);
   const uint32_t Rp = (uint32_t)(d.Rw - d.S);
-  return (wp * (uint32_t)d.C + Pp - 1) / Pp - (wp < Rp ? wp : Rp) * (uint32_t)d.D;
+  return fdiv(wp * (uint32_t)d.C + Pp - 1, d.by_pp) - (wp < Rp ? wp : Rp) * (uint32_t)d.D;
 }
 // First row unit of workgroup w (WU for w == P), moved to an even block.
 __host__ __device__ inline uint32_t row_begin(const DecodeSplit& d, int w) {
   uint32_t b = row_begin_raw(d, w);
-  if (b > 0 && b < split_wu(d) && (b % (uint32_t)d.KB) % 2 == 1) ++b;
+  if (b > 0 && b < split_wu(d) && fmod(b, d.by_kb) % 2 == 1) ++b;
   return b;
 }
 // Workgroup whose row run holds row unit u: the largest w with
@@ -96,10 +127,10 @@ __host__ __device__ inline int row_owner(const DecodeSplit& d, uint32_t u) {
 
 // Partial-sum slot of workgroup w for row band `band` / rank band `rb`.
 __host__ __device__ inline int row_slot(const DecodeSplit& d, int w, int band) {
-  return 2 * w + (row_begin(d, w) / (uint32_t)d.KB == (uint32_t)band ? 0 : 1);
+  return 2 * w + (fdiv(row_begin(d, w), d.by_kb) == (uint32_t)band ? 0 : 1);
 }
 __host__ __device__ inline int rank_slot(const DecodeSplit& d, int w, int rb) {
-  return 2 * d.P + 2 * w + (rank_begin(d, w) / (uint32_t)d.KB == (uint32_t)rb ? 0 : 1);
+  return 2 * d.P + 2 * w + (fdiv(rank_begin(d, w), d.by_kb) == (uint32_t)rb ? 0 : 1);
 }
 __host__ __device__ inline int split_slots(const DecodeSplit& d) { return 4 * d.P; }
 
@@ -112,8 +143,17 @@ constexpr int kRankUnitsPerWg = 8;
 constexpr int kRankUnitCost2 = 5;   // twice the row-unit equivalents of one rank unit
 constexpr int kRankFixedCost = 4;
 
+inline DecodeSplit with_divisors(DecodeSplit d) {
+  const uint32_t RU = split_ru(d);
+  d.by_kb = make_fastdiv((uint32_t)d.KB);
+  d.by_pp = make_fastdiv((uint32_t)(d.P - d.S));
+  d.by_rw = make_fastdiv(d.Rw > 0 ? (uint32_t)d.Rw : 1u);
+  d.by_ru = make_fastdiv(RU > 0 ? RU : 1u);
+  return d;
+}
+
 // The split for P_max = slots workgroups.  Host only.
-inline DecodeSplit make_split(int KB, int RB, int NB, int slots) {
+inline DecodeSplit make_split_plain(int KB, int RB, int NB, int slots) {
   DecodeSplit d;
   d.KB = KB;
   d.RB = RB;
@@ -131,9 +171,9 @@ inline DecodeSplit make_split(int KB, int RB, int NB, int slots) {
   if (Rw > slots) Rw = slots;
   const long long upw = (RU + Rw - 1) / Rw;
   const long long D = (kRankUnitCost2 * upw + 1) / 2 + kRankFixedCost;
-  // shared: floor(C / P) >= 2 D + 2, so a rank workgroup keeps at least as
-  // many row units as its rank units stand for (and two at least)
-  long long p_sh = (WU + Rw * D) / (2 * D + 2);
+  // shared: floor(C / (P - 1)) >= 2 D + 2, so a rank workgroup keeps at
+  // least as many row units as its rank units stand for (and two at least)
+  long long p_sh = 1 + (WU + (Rw - 1) * D) / (2 * D + 2);
   if (p_sh > slots) p_sh = slots;
   // separate: Rw rank workgroups, then P - Rw >= 1 row workgroups of >= 2
   // units each (fewer rank workgroups if the slots run out)
@@ -143,12 +183,12 @@ inline DecodeSplit make_split(int KB, int RB, int NB, int slots) {
   const long long rw_sh = (RU + kRankUnitsPerWg - 1) / kRankUnitsPerWg < slots
                               ? (RU + kRankUnitsPerWg - 1) / kRankUnitsPerWg
                               : slots;
-  if (p_sh >= rw_sh && (Rw < 1 || p_sh >= p_sep)) {
-    d.S = 0;
+  if (p_sh >= rw_sh && p_sh >= 2 && (Rw < 1 || p_sh >= p_sep)) {
+    d.S = 1;
     d.P = (int)p_sh;
     d.D = (int)D;
     d.Rw = (int)rw_sh;
-    d.C = (int)(WU + rw_sh * D);
+    d.C = (int)(WU + (rw_sh - 1) * D);
   } else if (Rw >= 1) {
     d.S = (int)Rw;
     d.Rw = (int)Rw;
@@ -163,6 +203,10 @@ inline DecodeSplit make_split(int KB, int RB, int NB, int slots) {
     d.C = (int)WU;
   }
   return d;
+}
+
+inline DecodeSplit make_split(int KB, int RB, int NB, int slots) {
+  return with_divisors(make_split_plain(KB, RB, NB, slots));
 }
 
 // Partial-sum slots a workspace holds for a layer: enough for the split at

@@ -28,6 +28,24 @@ static char g_msg[512];
 
 extern "C" const char* check_message() { return g_msg; }
 
+// FastDiv against the divider for divisors 1 .. dmax and numerators below
+// 2^31 (all small ones, then a stride through the range and its top end).
+extern "C" int check_fastdiv(uint32_t dmax) {
+  g_msg[0] = 0;
+  for (uint32_t d = 1; d <= dmax; ++d) {
+    const FastDiv f = make_fastdiv(d);
+    for (uint32_t n = 0; n < 4096; ++n)
+      REQUIRE(fdiv(n, f) == n / d && fmod(n, f) == n % d, "fdiv(%u, %u)", n, d);
+    for (uint64_t n = 4096; n < (1ull << 31); n += 7919 * (uint64_t)d + 104729)
+      REQUIRE(fdiv((uint32_t)n, f) == (uint32_t)n / d, "fdiv(%llu, %u)", (unsigned long long)n, d);
+    for (uint32_t k = 0; k < 64; ++k) {
+      const uint32_t n = (1u << 31) - 1 - k;
+      REQUIRE(fdiv(n, f) == n / d, "fdiv(%u, %u)", n, d);
+    }
+  }
+  return 0;
+}
+
 // 0 = all checks hold; otherwise g_msg says which failed.  stats (may be
 // NULL): P, Rw, S, D, max segments of a row band, max segments of a rank
 // band, workspace slots, max row units of one workgroup.
@@ -38,7 +56,9 @@ extern "C" int check_split(int KB, int RB, int NB, int slots, int max_slots, lon
   const long long RU = split_ru(d), WU = split_wu(d);
   REQUIRE(d.KB == KB && d.RB == RB && d.NB == NB, "split fields");
   REQUIRE(d.P >= 1 && d.P <= (slots < 1 ? 1 : slots), "P=%d outside [1, %d]", d.P, slots);
-  REQUIRE(d.S == 0 || d.S == d.Rw, "S=%d Rw=%d", d.S, d.Rw);
+  // rank work: workgroup 0 reduces it and takes no rows, unless it is alone
+  REQUIRE(RB == 0 ? d.S == 0 : (d.P == 1 ? d.S == 0 : (d.S == 1 || d.S == d.Rw)),
+          "S=%d Rw=%d P=%d", d.S, d.Rw, d.P);
   REQUIRE(RB == 0 ? d.Rw == 0 : (d.Rw >= 1 && d.Rw <= d.P && d.Rw <= RU), "Rw=%d", d.Rw);
   REQUIRE(d.S < d.P, "no workgroup takes rows (S=%d P=%d)", d.S, d.P);
 

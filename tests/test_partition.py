@@ -33,7 +33,14 @@ def lib():
     L.check_split.argtypes = [ctypes.c_int] * 5 + [ctypes.POINTER(ctypes.c_longlong)]
     L.check_split.restype = ctypes.c_int
     L.check_message.restype = ctypes.c_char_p
+    L.check_fastdiv.argtypes = [ctypes.c_uint32]
+    L.check_fastdiv.restype = ctypes.c_int
     return L
+
+
+def test_fast_division_matches_the_divider(lib):
+    # the split divides by fixed values with a multiply and a shift
+    assert lib.check_fastdiv(1100) == 0, lib.check_message().decode()
 
 
 def run(lib, K, N, r, slots):
@@ -71,9 +78,9 @@ def test_benchmark_layers_fill_the_device(lib, K, N, r):
 
 def test_the_70b_layer_shares_rank_workgroups_with_rows(lib):
     # 28672 -> 8192: a rank workgroup's eight rank units are a small part of
-    # its share, so it goes on to stream rows (shared mode)
+    # its share, so all but the reducing workgroup 0 go on to stream rows
     st = run(lib, 28672, 8192, 64, 256)
-    assert st["S"] == 0 and st["D"] > 0, st
+    assert st["S"] == 1 and st["D"] > 0, st
 
 
 def test_small_layers_keep_rank_workgroups_apart(lib):
