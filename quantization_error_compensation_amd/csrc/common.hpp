@@ -203,6 +203,33 @@ __device__ __forceinline__ uint32_t bload2(rsrc_t r, uint32_t voff, uint32_t sof
   return (uint32_t)(uint16_t)__builtin_amdgcn_raw_buffer_load_b16(r, voff, soff, 0);
 }
 
+// Bring the whole kernel-argument block of the running kernel (Bytes long)
+// into the scalar cache with one memory round trip: one 4-byte scalar load
+// per 64-byte line, all issued before a single wait in the same asm block (so
+// no load is left in flight past it).  Without it the compiler fetches the
+// argument fields where it first needs them, one line after another, each
+// a cache miss waited for before the next (some 2 us at a kernel's start).
+template <int Bytes>
+__device__ __forceinline__ void warm_kernel_args() {
+  static_assert(Bytes >= 4 && Bytes <= 384, "argument block size");
+  const auto kp = __builtin_amdgcn_kernarg_segment_ptr();
+  uint32_t a, b, c, d, e, f, g;
+  asm volatile(
+      "s_load_dword %0, %7, 0x0\n\t"
+      "s_load_dword %1, %7, %8\n\t"
+      "s_load_dword %2, %7, %9\n\t"
+      "s_load_dword %3, %7, %10\n\t"
+      "s_load_dword %4, %7, %11\n\t"
+      "s_load_dword %5, %7, %12\n\t"
+      "s_load_dword %6, %7, %13\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=s"(a), "=s"(b), "=s"(c), "=s"(d), "=s"(e), "=s"(f), "=s"(g)
+      : "s"(kp), "n"(Bytes > 0x40 ? 0x40 : 0), "n"(Bytes > 0x80 ? 0x80 : 0),
+        "n"(Bytes > 0xC0 ? 0xC0 : 0), "n"(Bytes > 0x100 ? 0x100 : 0),
+        "n"(Bytes > 0x140 ? 0x140 : 0), "n"((Bytes - 4) & ~3)
+      : "memory");
+}
+
 // Index of the calling wave in its workgroup as a wave-uniform value, so that
 // offsets derived from it stay in scalar registers (a buffer load whose scalar
 // offset the compiler cannot prove uniform is wrapped in a per-lane loop).

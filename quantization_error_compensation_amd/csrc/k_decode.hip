@@ -845,6 +845,7 @@ __device__ void reduce_ranks(const DecodeParams& p, uint8_t* xlds, int* s_flag) 
 // stages stay in registers.
 template <int MT, bool GROUPED>
 __global__ __launch_bounds__(kThreads, W * kDecodeOccupancy / 4) void decode_kernel(DecodeParams p) {
+  warm_kernel_args<sizeof(DecodeParams)>();
   // x buffers (also the MLP gate's working area, T (r + h) + max(r, h) floats)
   static_assert(2 * Burst<MT>::kBuf / 4 >= 16 * MT * 256 + 128, "MLP gate LDS");
   __shared__ __attribute__((aligned(16))) uint8_t xlds[2 * Burst<MT>::kBuf];

@@ -75,6 +75,7 @@ static_assert(kPrefillWaves == 8 && kPrefillBN == 256 && kPrefillBM == 128, "til
 
 template <bool GROUPED>
 __global__ __launch_bounds__(512, 1) void prefill_kernel(PrefillParams p) {
+  warm_kernel_args<sizeof(PrefillParams)>();
   __shared__ __attribute__((aligned(16))) uint8_t smem[kStages * kStage];
   __shared__ int s_last;
 

@@ -47,6 +47,7 @@ struct ProjParams {
 
 template <int RTX>  // RTX = r / 16 rank tiles
 __global__ __launch_bounds__(256, 2) void projection_kernel(ProjParams p) {
+  warm_kernel_args<sizeof(ProjParams)>();
   constexpr int MT = 2;                  // 32 tokens = two 16-row MFMA tiles
   constexpr int RA = RTX > 0 ? RTX : 1;  // array extent (rank 0 still sums x)
   __shared__ float red[4][MT][RTX + 1][4][64];
@@ -133,6 +134,7 @@ __global__ __launch_bounds__(256, 2) void projection_kernel(ProjParams p) {
 }
 
 __global__ __launch_bounds__(256) void finish_kernel(ProjParams p) {
+  warm_kernel_args<sizeof(ProjParams)>();
   const int R1 = p.r + 1;
   const int e = blockIdx.x * 256 + threadIdx.x;
   if (e >= p.T * R1) return;
