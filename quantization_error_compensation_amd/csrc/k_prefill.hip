@@ -105,7 +105,9 @@ __global__ __launch_bounds__(512, 1) void prefill_kernel(PrefillParams p) {
   // multiple of 16, so rows_n * G * 2 is a multiple of 4 and the word never
   // reaches past the tile's last scale.
   const u32x4 sr = sdesc(p.scales + (size_t)n0 * p.G, (uint32_t)rows_n * p.G * 2);
-  const u32x4 zr = p.has_z ? sdesc(p.zeros + (size_t)n0 * p.ZW, (uint32_t)rows_n * p.ZW * 4) : sr;
+  // Without zero-points the view is empty: its loads read zero words.
+  const u32x4 zr = p.has_z ? sdesc(p.zeros + (size_t)n0 * p.ZW, (uint32_t)rows_n * p.ZW * 4)
+                           : sdesc(p.scales, 0u);
   const u32x4 gr = sdesc(p.sblk, (uint32_t)KB * p.Tp * 8);
   const uint32_t lds0 = lds_addr(smem);
 
@@ -146,18 +148,76 @@ __global__ __launch_bounds__(512, 1) void prefill_kernel(PrefillParams p) {
         tot[a][b][v] = 0.f;
       }
 
-  auto compute = [&](int stage, int kb) {
-    const uint8_t* X = smem + stage * kStage;
-    const uint8_t* W = X + kXStage;
-    const uint8_t* M = W + kWStage;
-    u32x4 wd[2][2];
+  // Fragment reads from a stage.  A lane's code words: row n of its 32-row
+  // slice, 16-byte pieces 2q and 2q + 1 (K steps 0-3 and 4-7).
+  auto read_w = [&](const uint8_t* W, u32x4 (&wd)[2][2]) {
     for (int ns = 0; ns < 2; ++ns) {
       const int n = wn * 64 + ns * 32 + i32;
       const int sw = (n >> 2) & 3;
       wd[ns][0] = *reinterpret_cast<const u32x4*>(W + n * 64 + ((2 * q) ^ sw) * 16);
       wd[ns][1] = *reinterpret_cast<const u32x4*>(W + n * 64 + ((2 * q + 1) ^ sw) * 16);
     }
-    float sc[2];
+  };
+  auto read_x = [&](const uint8_t* X, int s, u32x4 (&xa)[2]) {
+    for (int ms = 0; ms < 2; ++ms) {
+      const int t = wm * 64 + ms * 32 + i32;
+      xa[ms] = *reinterpret_cast<const u32x4*>(X + t * 256 + ((8 * q + s) ^ (t & 15)) * 16);
+    }
+  };
+  auto step = [&](const u32x4 (&xa)[2], uint32_t w0, uint32_t w1) {
+    const u32x4 wb0 = codes_to_bf16_offset_natural(w0);
+    const u32x4 wb1 = codes_to_bf16_offset_natural(w1);
+    for (int ms = 0; ms < 2; ++ms) {
+      acc[ms][0] = mfma32x32x16(xa[ms], wb0, acc[ms][0]);
+      acc[ms][1] = mfma32x32x16(xa[ms], wb1, acc[ms][1]);
+    }
+  };
+  auto fold = [&](const float (&sc)[2]) {
+    for (int ms = 0; ms < 2; ++ms)
+      for (int ns = 0; ns < 2; ++ns)
+        for (int v = 0; v < 16; ++v) tot[ms][ns][v] = fmaf(sc[ns], acc[ms][ns][v], tot[ms][ns][v]);
+  };
+
+  // K loop over the 3-stage ring.  At the top of iteration kb this wave's
+  // loads of blocks kb and kb + 1 are in flight (8 each); waiting until at
+  // most 8 remain completes block kb, and the barrier makes every wave's part
+  // of it visible.  Past the barrier every wave has finished reading block
+  // kb - 1, so its stage takes the loads of block kb + 2.  Past the last
+  // block the loads repeat block kb1 - 1 into the free stage, which keeps the
+  // count of loads in flight the same in every iteration.
+  //
+  // The pipeline is rotated by one K step: the operands of block kb - 1's
+  // last step (its activations and code words) and its scales are read
+  // before the barrier and carried in registers, so that its last four
+  // matrix-core steps and its scale fold run after the barrier, while the
+  // first reads of block kb are in flight.
+  const uint32_t zxor = p.has_z ? 0u : 0x88888888u;
+  // lanes of the upper half hold K = 8..15 of the offset step: zero there
+  // (a mask, not a branch, so the reads stay ahead of their waits)
+  const uint32_t qmask = q == 0 ? 0xFFFFFFFFu : 0u;
+  issue(kb0, 0);
+  issue(min(kb0 + 1, kb1 - 1), 1);
+  u32x4 xc[2] = {u32x4{0u, 0u, 0u, 0u}, u32x4{0u, 0u, 0u, 0u}};  // carried: x of step 7
+  uint32_t wc[2] = {0u, 0u};                                     // carried: code words of step 7
+  float scc[2] = {0.f, 0.f};                                     // carried: scales
+  for (int kb = kb0; kb < kb1; ++kb) {
+    const int i = kb - kb0;
+    wait_vmcnt<kLoadsPerBlock>();
+    // lgkmcnt(0) through the builtin (0xC07F: vmcnt and expcnt at their
+    // maxima), which the compiler's own wait insertion sees: the carried
+    // step-7 operands then count as arrived.
+    __builtin_amdgcn_s_waitcnt(0xC07F);
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    issue(min(kb + 2, kb1 - 1), (i + 2) % kStages);
+
+    const uint8_t* X = smem + (i % kStages) * kStage;
+    const uint8_t* W = X + kXStage;
+    const uint8_t* M = W + kWStage;
+    u32x4 wd[2][2];
+    read_w(W, wd);
+    float sc[2] = {0.f, 0.f};
+    u32x4 xo[2], wo[2];
     if constexpr (GROUPED) {
       // Offset step: P starts at -(128 + z) * sum_x through one extra K = 16
       // matrix-core step whose only non-zero terms are the three bf16 parts
@@ -165,63 +225,59 @@ __global__ __launch_bounds__(512, 1) void prefill_kernel(PrefillParams p) {
       // side); then P gathers the eight code steps and is folded with s.
       const uint32_t* Ms = reinterpret_cast<const uint32_t*>(M + kMScale);
       const uint32_t* Mz = reinterpret_cast<const uint32_t*>(M + kMZero);
-      u32x4 xo[2], wo[2];
       for (int ms = 0; ms < 2; ++ms) {
         const int t = wm * 64 + ms * 32 + i32;
         const u32x2 sx = *reinterpret_cast<const u32x2*>(M + kMSum + t * 8);
-        xo[ms] = q == 0 ? u32x4{sx.x, sx.y, 0u, 0u} : u32x4{0u, 0u, 0u, 0u};
+        xo[ms] = u32x4{sx.x & qmask, sx.y & qmask, 0u, 0u};
       }
       for (int ns = 0; ns < 2; ++ns) {
         const int n = wn * 64 + ns * 32 + i32;
         const uint32_t sword = Ms[n];
         const uint32_t sbits = (((n0 + n) * p.G + kb) & 1) ? (sword >> 16) : (sword & 0xFFFFu);
         sc[ns] = half_bits_to_f32((uint16_t)sbits);
-        const uint32_t z = p.has_z ? (Mz[n] >> (4 * (kb & 7))) & 15u : 8u;
+        // without zero-points the word reads as zero and z = 8 comes from
+        // the xor (one path, so no branch splits the read from its wait)
+        const uint32_t z = ((Mz[n] ^ zxor) >> (4 * (kb & 7))) & 15u;
         const uint32_t mzb = 0xC300u | z;  // bf16 bits of -(128 + z)
-        wo[ns] = q == 0 ? u32x4{mzb | (mzb << 16), mzb, 0u, 0u} : u32x4{0u, 0u, 0u, 0u};
+        wo[ns] = u32x4{(mzb | (mzb << 16)) & qmask, mzb & qmask, 0u, 0u};
       }
+    }
+    u32x4 xa[2];
+    read_x(X, 0, xa);
+
+    // Block kb - 1: its last K step and its fold.
+    if (i > 0) {
+      step(xc, wc[0], wc[1]);
+      if constexpr (GROUPED) fold(scc);
+    }
+
+    // Block kb: the offset step, then K steps 0-6; step 7's operands are
+    // read here and carried.
+    if constexpr (GROUPED) {
       f32x16 zero;
       for (int v = 0; v < 16; ++v) zero[v] = 0.f;
       for (int ms = 0; ms < 2; ++ms)
         for (int ns = 0; ns < 2; ++ns) acc[ms][ns] = mfma32x32x16(xo[ms], wo[ns], zero);
     }
 #pragma unroll
-    for (int s = 0; s < 8; ++s) {
-      u32x4 xa[2], wb[2];
-      for (int ms = 0; ms < 2; ++ms) {
-        const int t = wm * 64 + ms * 32 + i32;
-        xa[ms] = *reinterpret_cast<const u32x4*>(X + t * 256 + ((8 * q + s) ^ (t & 15)) * 16);
-      }
-      for (int ns = 0; ns < 2; ++ns) wb[ns] = codes_to_bf16_offset_natural(wd[ns][s >> 2][s & 3]);
-      for (int ms = 0; ms < 2; ++ms)
-        for (int ns = 0; ns < 2; ++ns) acc[ms][ns] = mfma32x32x16(xa[ms], wb[ns], acc[ms][ns]);
+    for (int s = 0; s < 7; ++s) {
+      u32x4 xn[2];
+      read_x(X, s + 1, xn);
+      step(xa, wd[0][s >> 2][s & 3], wd[1][s >> 2][s & 3]);
+      xa[0] = xn[0];
+      xa[1] = xn[1];
     }
-    if constexpr (GROUPED) {
-      for (int ms = 0; ms < 2; ++ms)
-        for (int ns = 0; ns < 2; ++ns)
-          for (int v = 0; v < 16; ++v) tot[ms][ns][v] = fmaf(sc[ns], acc[ms][ns][v], tot[ms][ns][v]);
-    }
-  };
-
-  // K loop over the 3-stage ring.  At the top of iteration kb this wave's
-  // loads of blocks kb and kb + 1 are in flight (8 each); waiting until at
-  // most 8 remain completes block kb, and the barrier makes every wave's part
-  // of it visible.  Past the barrier every wave has finished block kb - 1, so
-  // its stage takes the loads of block kb + 2.  Past the last block the loads
-  // repeat block kb1 - 1 into the free stage, which keeps the count of loads
-  // in flight the same in every iteration.
-  issue(kb0, 0);
-  issue(min(kb0 + 1, kb1 - 1), 1);
-  for (int kb = kb0; kb < kb1; ++kb) {
-    const int i = kb - kb0;
-    wait_vmcnt<kLoadsPerBlock>();
-    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-    __builtin_amdgcn_s_barrier();
-    asm volatile("" ::: "memory");
-    issue(min(kb + 2, kb1 - 1), (i + 2) % kStages);
-    compute(i % kStages, kb);
+    xc[0] = xa[0];
+    xc[1] = xa[1];
+    wc[0] = wd[0][1][3];
+    wc[1] = wd[1][1][3];
+    scc[0] = sc[0];
+    scc[1] = sc[1];
   }
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  // The last block's last step and fold.
+  step(xc, wc[0], wc[1]);
+  if constexpr (GROUPED) fold(scc);
 
   if constexpr (!GROUPED) {
     for (int ms = 0; ms < 2; ++ms)
