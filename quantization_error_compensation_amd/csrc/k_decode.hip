@@ -29,8 +29,11 @@
 //     the matrix-core K order and written to a double-buffered LDS area with
 //     the block sums of x (vector adds and a 16-lane DPP tree); one barrier
 //     per burst publishes both to all waves;
-//   * codes: 16 bytes per lane per block (16 rows x 64 B per instruction);
-//     bf16 operands 128 + c by byte permutes;
+//   * codes: 16 bytes per lane per block, four consecutive lanes reading a
+//     row's 64 contiguous bytes (16 rows x 64 B per instruction: lanes that
+//     read 16 different rows slowed the address unit), turned into the
+//     matrix-core layout (lane = row) through a wave-private LDS area when
+//     the burst computes; bf16 operands 128 + c by byte permutes;
 //   * group scale and zero-point word of the lane's row: one small load each
 //     per block, straight into registers;
 //   * matrix cores 16x16x32: tokens (padded to 16 or 32) x 16 rows x 32 K;
@@ -351,9 +354,15 @@ struct RowStage {
 // y with the scales applied.  Per block and token the result is
 // s (P - (128 + z) S), P the matrix-core product with the 128 + c operands
 // and S the block sum of x.
+// A wave's code area: [block of the burst][16 rows][64 B]; 16-byte piece q
+// of row r sits at position q ^ code_swz(r), so that the writes (four lanes
+// per row) and the reads (one lane per row) both spread over the banks.
+__device__ __forceinline__ int code_swz(int r) { return ((r >> 1) ^ (r >> 2)) & 3; }
+constexpr int kCodeArea = 4 * 1024;  // bytes per wave: up to four blocks
+
 template <int MT, bool GROUPED>
 __device__ void row_segment(const DecodeParams& p, int band, int lo, int hi, uint8_t* xlds,
-                            uint8_t* mlds, int& burst, f32x4 (&yo)[MT]) {
+                            uint8_t* mlds, uint8_t* clds, int& burst, f32x4 (&yo)[MT]) {
   constexpr int NS = Burst<MT>::kRow;
   constexpr uint32_t kOut = 0x80000000u;
   const int lane = threadIdx.x & 63, wave = wave_id(), q = lane >> 4, c16 = lane & 15;
@@ -362,7 +371,11 @@ __device__ void row_segment(const DecodeParams& p, int band, int lo, int hi, uin
   const int rc = min(band * BR + 16 * wave, p.N - 16);
   const uint32_t wrowB = (uint32_t)p.K / 2;
   const rsrc_t wr = make_rsrc(p.wq + (size_t)rc * (p.K / 8), 16u * wrowB);
-  const uint32_t wo = (uint32_t)c16 * wrowB + 16u * q;
+  // load layout: lane 4 r + j reads piece j of row r
+  const int lr = lane >> 2, lj = lane & 3;
+  const uint32_t wo = (uint32_t)lr * wrowB + 16u * lj;
+  uint8_t* cl = clds + wave * kCodeArea;
+  static_assert(NS * 1024 <= kCodeArea, "code area");
   const rsrc_t sr = make_rsrc(p.scales + (size_t)rc * p.G, 16u * p.G * 2);
   const rsrc_t zr = make_rsrc(p.zeros + (size_t)rc * p.ZW, p.has_z ? 16u * p.ZW * 4 : 0u);
   using M = Meta<MT>;
@@ -404,6 +417,8 @@ __device__ void row_segment(const DecodeParams& p, int band, int lo, int hi, uin
     const float* sums = reinterpret_cast<const float*>(buf + Burst<MT>::kSums);
     ++burst;
     x_store<MT, NS, true>(buf, wave, lane, s.x);
+    for (int i = 0; i < NS; ++i)
+      *reinterpret_cast<u32x4*>(cl + i * 1024 + lr * 64 + ((lj ^ code_swz(lr)) * 16)) = s.w[i];
     lds_barrier();
     const int k = (b - lo) / NS, j = k / 16;  // this burst's chunk
     uint32_t meta[NS];  // packed words of blocks b .. b + NS - 1 for row c16
@@ -426,10 +441,12 @@ __device__ void row_segment(const DecodeParams& p, int band, int lo, int hi, uin
       x_frags<MT>(buf, i, lane, xf[i]);
       for (int mt = 0; mt < MT; ++mt)
         sb[i][mt] = *reinterpret_cast<const f32x4*>(sums + i * 16 * MT + 16 * mt + 4 * q);
-      wb[i][0] = codes_to_bf16_offset(s.w[i].x);
-      wb[i][1] = codes_to_bf16_offset(s.w[i].y);
-      wb[i][2] = codes_to_bf16_offset(s.w[i].z);
-      wb[i][3] = codes_to_bf16_offset(s.w[i].w);
+      const u32x4 cw =
+          *reinterpret_cast<const u32x4*>(cl + i * 1024 + c16 * 64 + ((q ^ code_swz(c16)) * 16));
+      wb[i][0] = codes_to_bf16_offset(cw.x);
+      wb[i][1] = codes_to_bf16_offset(cw.y);
+      wb[i][2] = codes_to_bf16_offset(cw.z);
+      wb[i][3] = codes_to_bf16_offset(cw.w);
     }
     if constexpr (GROUPED) {
       f32x4 P[NS][MT];
@@ -850,6 +867,7 @@ __global__ __launch_bounds__(kThreads, W * kDecodeOccupancy / 4) void decode_ker
   static_assert(2 * Burst<MT>::kBuf / 4 >= 16 * MT * 256 + 128, "MLP gate LDS");
   __shared__ __attribute__((aligned(16))) uint8_t xlds[2 * Burst<MT>::kBuf];
   __shared__ __attribute__((aligned(16))) uint8_t mlds[GROUPED ? W * Meta<MT>::kWave : 16];
+  __shared__ __attribute__((aligned(16))) uint8_t clds[W * kCodeArea];
   __shared__ int s_last, s_wait;
   const int tid = threadIdx.x;
   const int wg = blockIdx.x;
@@ -886,7 +904,7 @@ __global__ __launch_bounds__(kThreads, W * kDecodeOccupancy / 4) void decode_ker
     const int nseg = row_owner(sp, bend - 1) - first + 1;
 
     f32x4 v[MT];
-    row_segment<MT, GROUPED>(p, band, lo, hi, xlds, mlds, burst, v);
+    row_segment<MT, GROUPED>(p, band, lo, hi, xlds, mlds, clds, burst, v);
     if (nseg > 1 && !arrive<MT>(p, band, first, nseg, &s_last, v)) continue;
     if (p.r > 0) {
       u32x4 bfr[kRankSteps];
