@@ -360,9 +360,12 @@ struct RowStage {
 __device__ __forceinline__ int code_swz(int r) { return ((r >> 1) ^ (r >> 2)) & 3; }
 constexpr int kCodeArea = 4 * 1024;  // bytes per wave: up to four blocks
 
-template <int MT, bool GROUPED>
+// mid() runs while the segment's first loads are in flight (scalar work
+// that the segment does not need).
+template <int MT, bool GROUPED, class Mid>
 __device__ void row_segment(const DecodeParams& p, int band, int lo, int hi, uint8_t* xlds,
-                            uint8_t* mlds, uint8_t* clds, int& burst, f32x4 (&yo)[MT]) {
+                            uint8_t* mlds, uint8_t* clds, int& burst, f32x4 (&yo)[MT],
+                            Mid&& mid) {
   constexpr int NS = Burst<MT>::kRow;
   constexpr uint32_t kOut = 0x80000000u;
   const int lane = threadIdx.x & 63, wave = wave_id(), q = lane >> 4, c16 = lane & 15;
@@ -495,9 +498,11 @@ __device__ void row_segment(const DecodeParams& p, int band, int lo, int hi, uin
     for (int n = 0; n < 16; ++n) m0s[n] = meta_scale(n, blk);
     for (int n = 0; n < 16; ++n) m0z[n] = meta_zero(n, blk);
     issue(s0, lo);
+    mid();
     for (int n = 0; n < 16; ++n) *mp_at(0, n, ment) = meta_pack(m0s[n], m0z[n], blk, p.has_z);
   } else {
     issue(s0, lo);
+    mid();
   }
   pipeline2(lo, hi, NS, s0, s1, issue, consume);
 
@@ -900,11 +905,16 @@ __global__ __launch_bounds__(kThreads, W * kDecodeOccupancy / 4) void decode_ker
     const int lo = (int)(u - bbeg);
     const int hi = (int)(min(u1, bend) - bbeg);
     u = min(u1, bend);
-    const int first = row_owner(sp, bbeg);
-    const int nseg = row_owner(sp, bend - 1) - first + 1;
+    // the owners of the band's first and last units (a search over the
+    // split) while the segment's first loads are in flight
+    int first = 0, nseg = 1;
+    auto owners = [&]() {
+      first = row_owner(sp, bbeg);
+      nseg = row_owner(sp, bend - 1) - first + 1;
+    };
 
     f32x4 v[MT];
-    row_segment<MT, GROUPED>(p, band, lo, hi, xlds, mlds, clds, burst, v);
+    row_segment<MT, GROUPED>(p, band, lo, hi, xlds, mlds, clds, burst, v, owners);
     if (nseg > 1 && !arrive<MT>(p, band, first, nseg, &s_last, v)) continue;
     if (p.r > 0) {
       u32x4 bfr[kRankSteps];

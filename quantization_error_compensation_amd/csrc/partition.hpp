@@ -79,6 +79,7 @@ struct DecodeSplit {
   int D;        // row-unit equivalents a rank workgroup's rank units stand for (shared)
   int C;        // the row cost axis: WU + (Rw - S) D (shared mode)
   FastDiv by_kb, by_pp, by_rw, by_ru;  // KB, P - S, Rw, RU (1 when zero)
+  FastDiv by_c, by_cd;                 // C, C - (P - S) D (the owner estimate)
 };
 
 __host__ __device__ inline uint32_t split_ru(const DecodeSplit& d) {
@@ -114,8 +115,23 @@ __host__ __device__ inline uint32_t row_begin(const DecodeSplit& d, int w) {
   return b;
 }
 // Workgroup whose row run holds row unit u: the largest w with
-// row_begin(w) <= u (runs from S on are never empty).
+// row_begin(w) <= u (runs from S on are never empty).  Without the
+// even-block move, row_begin_raw(S + w') <= u reads, for w' >= Rp - S,
+// w' C / P' <= u + (Rw - S) D, and below, w' (C - P' D) / P' <= u (the
+// ceilings drop out against the integer u); the largest such w' is one
+// division.  The move adds at most one unit, so the owner is that estimate
+// or the workgroup before it.
 __host__ __device__ inline int row_owner(const DecodeSplit& d, uint32_t u) {
+  const uint32_t Pp = (uint32_t)(d.P - d.S);
+  const uint32_t Rp = (uint32_t)(d.Rw - d.S);
+  uint32_t wp = fdiv((u + Rp * (uint32_t)d.D) * Pp, d.by_c);
+  if (wp < Rp) wp = fdiv(u * Pp, d.by_cd);
+  int w = d.S + (int)(wp < Pp - 1 ? wp : Pp - 1);
+  if (w > d.S && row_begin(d, w) > u) --w;
+  return w;
+}
+// The search it replaces, for the host-side check.
+inline int row_owner_search(const DecodeSplit& d, uint32_t u) {
   int lo = d.S, hi = d.P - 1;
   while (lo < hi) {
     const int mid = (lo + hi + 1) >> 1;
@@ -149,6 +165,9 @@ inline DecodeSplit with_divisors(DecodeSplit d) {
   d.by_pp = make_fastdiv((uint32_t)(d.P - d.S));
   d.by_rw = make_fastdiv(d.Rw > 0 ? (uint32_t)d.Rw : 1u);
   d.by_ru = make_fastdiv(RU > 0 ? RU : 1u);
+  d.by_c = make_fastdiv(d.C > 0 ? (uint32_t)d.C : 1u);
+  const long long cd = (long long)d.C - (long long)(d.P - d.S) * d.D;
+  d.by_cd = make_fastdiv(cd > 0 ? (uint32_t)cd : 1u);
   return d;
 }
 
