@@ -200,6 +200,15 @@ __device__ __forceinline__ void x_frags(const uint8_t* buf, int i, int lane, u32
                                                  (4 * q + j) * 16);
 }
 
+// A wave's code area (4 KB of LDS), where loads made with consecutive lanes
+// along a row are turned into the matrix-core layout (one lane per row).
+// Row segments: [block of the burst][16 rows][64 B], 16-byte piece q of row
+// r at position q ^ code_swz(r); rank segments: [16 rows of A][256 B], piece
+// e of row r at position e ^ r.  Both spread the writes (consecutive lanes
+// along a row) and the reads (one lane per row) over the banks.
+__device__ __forceinline__ int code_swz(int r) { return ((r >> 1) ^ (r >> 2)) & 3; }
+constexpr int kCodeArea = 4 * 1024;  // bytes per wave: up to four blocks
+
 // ------------------------------------------------------------ rank segment
 // A barrier that leaves global loads in flight: only this wave's LDS writes
 // are awaited before the workgroup meets.
@@ -254,7 +263,7 @@ struct RankStage {
 // takes block b + f of the burst starting at b.
 template <int MT>
 __device__ void rank_segment(const DecodeParams& p, int rb, int lo, int hi, uint8_t* xlds,
-                             int& burst, f32x4 (&uo)[MT]) {
+                             uint8_t* clds, int& burst, f32x4 (&uo)[MT]) {
   constexpr int NS = Burst<MT>::kRank;
   static_assert(NS == PH, "one block per phase and burst");
   const int lane = threadIdx.x & 63, wave = wave_id(), q = lane >> 4, c16 = lane & 15;
@@ -264,7 +273,10 @@ __device__ void rank_segment(const DecodeParams& p, int rb, int lo, int hi, uint
   const int j0 = min(64 * rb + 16 * tile, p.r - 16);
   const uint32_t arowB = (uint32_t)p.K * 2;
   const rsrc_t ar = make_rsrc(p.A + (size_t)j0 * p.K, 16u * arowB);
-  const uint32_t ao = (uint32_t)c16 * arowB + 64u * q;  // pieces 4q .. 4q + 3 of row c16
+  // load layout: 16 consecutive lanes read a row's 256 B (rows lane / 16 + 4 j),
+  // turned into the matrix-core layout through the wave's code area
+  const uint32_t ao = (uint32_t)(lane >> 4) * arowB + 16u * (lane & 15);
+  uint8_t* cl = clds + wave * kCodeArea;
   for (int mt = 0; mt < MT; ++mt) uo[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   auto issue = [&](RankStage<MT, NS>& s, int b) {
@@ -272,19 +284,25 @@ __device__ void rank_segment(const DecodeParams& p, int rb, int lo, int hi, uint
     x_issue<MT, NS>(p, wave, lane, b, hi, live, s.x);
     const uint32_t av = b + ph < hi ? ao : 0x80000000u;
     for (int j = 0; j < 4; ++j)
-      s.a[j] = bload16(ar, av + 16 * j,
+      s.a[j] = bload16(ar, av + 4u * j * arowB,
                        __builtin_amdgcn_readfirstlane((uint32_t)min(b + ph, hi - 1) * 256));
   };
   auto consume = [&](RankStage<MT, NS>& s, int b) {
     uint8_t* buf = xlds + (burst & 1) * Burst<MT>::kBuf;
     ++burst;
     x_store<MT, NS, false>(buf, wave, lane, s.x);
+    for (int j = 0; j < 4; ++j) {  // piece e of row r at position e ^ r
+      const int r = (lane >> 4) + 4 * j;
+      *reinterpret_cast<u32x4*>(cl + r * 256 + (((lane & 15) ^ r) * 16)) = s.a[j];
+    }
     lds_barrier();
     {  // a block past the segment has x = 0 and A = 0: it adds nothing
       u32x4 xf[MT][4];
       x_frags<MT>(buf, ph, lane, xf);
       for (int j = 0; j < 4; ++j) {
-        const u32x4 ap = x_permute8(s.a[j]);
+        const u32x4 araw =
+            *reinterpret_cast<const u32x4*>(cl + c16 * 256 + (((4 * q + j) ^ c16) * 16));
+        const u32x4 ap = x_permute8(araw);
         for (int mt = 0; mt < MT; ++mt) uo[mt] = mfma16x16x32(xf[mt][j], ap, uo[mt]);
       }
     }
@@ -354,11 +372,6 @@ struct RowStage {
 // y with the scales applied.  Per block and token the result is
 // s (P - (128 + z) S), P the matrix-core product with the 128 + c operands
 // and S the block sum of x.
-// A wave's code area: [block of the burst][16 rows][64 B]; 16-byte piece q
-// of row r sits at position q ^ code_swz(r), so that the writes (four lanes
-// per row) and the reads (one lane per row) both spread over the banks.
-__device__ __forceinline__ int code_swz(int r) { return ((r >> 1) ^ (r >> 2)) & 3; }
-constexpr int kCodeArea = 4 * 1024;  // bytes per wave: up to four blocks
 
 // mid() runs while the segment's first loads are in flight (scalar work
 // that the segment does not need).
@@ -577,11 +590,9 @@ __device__ __forceinline__ void sum_parts(const DecodeParams& p, bool rank, int 
 // Finish a rank band: gate and publish alpha * v for this wave's 16 ranks
 // (with the MLP gate, which needs every rank of a token, publish u itself).
 template <int MT>
-__device__ void finish_rank(const DecodeParams& p, int rb, const f32x4 (&u)[MT]) {
-  const int lane = threadIdx.x & 63, wave = wave_id(), q = lane >> 4, c16 = lane & 15;
-  const int j = 64 * rb + 16 * wave + c16;
-  if (wave >= 4 || j >= p.r) return;  // u is in the waves of phase 0
-  const float g = p.gh > 0 ? 0.f : p.gv[j], b = p.gh > 0 ? 0.f : p.bv[j];
+__device__ void finish_rank(const DecodeParams& p, int j, float g, float b, const f32x4 (&u)[MT]) {
+  const int lane = threadIdx.x & 63, q = lane >> 4;
+  if (j >= p.r) return;
   const rsrc_t wr = make_rsrc(p.wv32, (uint32_t)p.T * p.r * 4);
   for (int mt = 0; mt < MT; ++mt)
     for (int i = 0; i < 4; ++i) {
@@ -817,23 +828,33 @@ __device__ __forceinline__ void post_rank_part(const DecodeParams& p, int rb, co
     __hip_atomic_fetch_add(&p.ctr[kCtrBand + rb], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// Workgroup 0: for each rank band, wait (bounded) until all its rank
-// workgroups have posted, sum their partials in workgroup order, gate and
-// publish alpha v (the MLP gate: u, then the gate pass over all ranks), and
-// raise the count the row finishers wait for.  A wait that gives up
-// publishes NaN and sets the error word.
+// Workgroup 0: wait (bounded) until every rank workgroup has posted, sum each
+// rank band's partials in workgroup order (the two bands of r > 64 at once,
+// one per half of the workgroup), gate and publish alpha v (the MLP gate: u,
+// then the gate pass over all ranks), and raise the count the row finishers
+// wait for.  A wait that gives up publishes NaN and sets the error word.
 template <int MT>
 __device__ void reduce_ranks(const DecodeParams& p, uint8_t* xlds, int* s_flag) {
   const DecodeSplit& sp = p.sp;
-  const int tid = threadIdx.x, col = 16 * wave_id() + (tid & 15);
-  for (int rb = 0; rb < p.RB; ++rb) {
-    const uint32_t bbeg = (uint32_t)rb * p.KB;
-    const int first = rank_owner(sp, bbeg);
-    const int nseg = rank_owner(sp, bbeg + p.KB - 1) - first + 1;
-    int* ctr = &p.ctr[kCtrBand + rb];
-    if (tid == 0) {
-      int spins = 0, ok = 1;
-      while (load_dev(ctr) < nseg) {
+  const int tid = threadIdx.x, wave = wave_id();
+  // With two rank bands each half of the workgroup reduces one, at the same
+  // time; with one, the first four waves do.  Lane: rank j of band rb.
+  const int rb = p.RB > 1 ? wave >> 2 : 0;
+  const bool active = p.RB > 1 || wave < 4;
+  const int col = 16 * (wave & 3) + (tid & 15);
+  const int j = 64 * rb + col;
+  // the gate's parameters, requested before the wait
+  float g = 0.f, b = 0.f;
+  if (p.gh == 0 && active && j < p.r) {
+    g = p.gv[j];
+    b = p.bv[j];
+  }
+  if (tid == 0) {
+    int spins = 0, ok = 1;
+    for (int k = 0; k < p.RB && ok; ++k) {
+      const uint32_t bbeg = (uint32_t)k * p.KB;
+      const int nseg = rank_owner(sp, bbeg + p.KB - 1) - rank_owner(sp, bbeg) + 1;
+      while (load_dev(&p.ctr[kCtrBand + k]) < nseg) {
         __builtin_amdgcn_s_sleep(1);
         if (++spins > kSpinLimit) {
           atomicOr(&p.ctr[kCtrError], 1);
@@ -841,18 +862,24 @@ __device__ void reduce_ranks(const DecodeParams& p, uint8_t* xlds, int* s_flag) 
           break;
         }
       }
-      *s_flag = ok;
     }
-    __syncthreads();
-    const bool ok = *s_flag != 0;
-    __syncthreads();
+    *s_flag = ok;
+  }
+  __syncthreads();
+  const bool ok = *s_flag != 0;
+  __syncthreads();
+  if (active) {
+    const uint32_t bbeg = (uint32_t)rb * p.KB;
+    const int first = rank_owner(sp, bbeg);
+    const int nseg = rank_owner(sp, bbeg + p.KB - 1) - first + 1;
     f32x4 v[MT];
-    if (wave_id() < 4) sum_parts<MT>(p, true, rb, first, nseg, col, v);
+    sum_parts<MT>(p, true, rb, first, nseg, col, v);
     if (!ok)
       for (int mt = 0; mt < MT; ++mt) v[mt] = f32x4{NAN, NAN, NAN, NAN};
-    if (tid == 0) store_dev(ctr, 0);
-    finish_rank<MT>(p, rb, v);
+    finish_rank<MT>(p, j, g, b, v);
   }
+  if (tid == 0)
+    for (int k = 0; k < p.RB; ++k) store_dev(&p.ctr[kCtrBand + k], 0);
   wait_vmem();
   __syncthreads();
   if (p.gh > 0) {
@@ -891,7 +918,7 @@ __global__ __launch_bounds__(kThreads, W * kDecodeOccupancy / 4) void decode_ker
       const int hi = (int)(min(u1, bend) - bbeg);
       u = min(u1, bend);
       f32x4 v[MT];
-      rank_segment<MT>(p, band, lo, hi, xlds, burst, v);
+      rank_segment<MT>(p, band, lo, hi, xlds, clds, burst, v);
       post_rank_part<MT>(p, band, v);
     }
     if (wg == 0 && p.RB > 0) reduce_ranks<MT>(p, xlds, &s_wait);
