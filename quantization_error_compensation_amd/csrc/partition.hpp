@@ -20,7 +20,9 @@
 // first go on to stream rows).  When the rank units would take more than
 // half of a workgroup's share (short row runs would cut bands into many
 // partial sums), the rank workgroups take no rows at all ("separate" mode,
-// S = Rw, D = 0) and the rows are split over the other P - Rw.  Row parts
+// S = Rw, D = 0) and the rows are split over the other P - Rw.  On the cost
+// axis each row band boundary takes X units (row_cost), so a run that
+// crosses one carries fewer units.  Row parts
 // start on an even block of their band, so the bursts' code loads stay on
 // 128-byte lines; every workgroup from S on keeps at least one row unit.
 //
@@ -77,9 +79,11 @@ struct DecodeSplit {
   int S;        // workgroups [0, S) take no row units: 1 (shared), Rw (separate), 0 (no
                 // rank units, or one workgroup)
   int D;        // row-unit equivalents a rank workgroup's rank units stand for (shared)
-  int C;        // the row cost axis: WU + (Rw - S) D (shared mode)
+  int X;        // cost of a row band boundary on the cost axis (row units)
+  int C;        // the row cost axis: WU + X (NB - 1) + (Rw - S) D
   FastDiv by_kb, by_pp, by_rw, by_ru;  // KB, P - S, Rw, RU (1 when zero)
   FastDiv by_c, by_cd;                 // C, C - (P - S) D (the owner estimate)
+  FastDiv by_kbx;                      // KB + X
 };
 
 __host__ __device__ inline uint32_t split_ru(const DecodeSplit& d) {
@@ -101,12 +105,27 @@ __host__ __device__ inline int rank_owner(const DecodeSplit& d, uint32_t u) {
   return (int)fdiv((u + 1) * (uint32_t)d.Rw + RU - 1, d.by_ru) - 1;
 }
 
-// First row unit of workgroup w on the cost axis, before alignment.
+// Row units on the cost axis: each band takes KB + X, its units then a gap of
+// X, so a run that crosses a band boundary pays X of its share (the arrival
+// and the next band's start cost a stream about that much), and a run
+// boundary that falls into a gap moves to the next band's start.
+__host__ __device__ inline uint32_t row_cost(const DecodeSplit& d, uint32_t u) {
+  if (d.X == 0) return u;
+  return u + (uint32_t)d.X * fdiv(u, d.by_kb);
+}
+__host__ __device__ inline uint32_t row_unit_at(const DecodeSplit& d, uint32_t c) {
+  if (d.X == 0) return c;
+  const uint32_t k = fdiv(c, d.by_kbx);
+  const uint32_t off = c - k * (uint32_t)(d.KB + d.X);
+  return k * (uint32_t)d.KB + (off < (uint32_t)d.KB ? off : (uint32_t)d.KB);
+}
+// First row unit of workgroup w, before alignment.
 __host__ __device__ inline uint32_t row_begin_raw(const DecodeSplit& d, int w) {
   const uint32_t wp = w > d.S ? (uint32_t)(w - d.S) : 0u;
   const uint32_t Pp = (uint32_t)(d.P - d.S);
   const uint32_t Rp = (uint32_t)(d.Rw - d.S);
-  return fdiv(wp * (uint32_t)d.C + Pp - 1, d.by_pp) - (wp < Rp ? wp : Rp) * (uint32_t)d.D;
+  return row_unit_at(d, fdiv(wp * (uint32_t)d.C + Pp - 1, d.by_pp) -
+                            (wp < Rp ? wp : Rp) * (uint32_t)d.D);
 }
 // First row unit of workgroup w (WU for w == P), moved to an even block.
 __host__ __device__ inline uint32_t row_begin(const DecodeSplit& d, int w) {
@@ -116,16 +135,18 @@ __host__ __device__ inline uint32_t row_begin(const DecodeSplit& d, int w) {
 }
 // Workgroup whose row run holds row unit u: the largest w with
 // row_begin(w) <= u (runs from S on are never empty).  Without the
-// even-block move, row_begin_raw(S + w') <= u reads, for w' >= Rp - S,
-// w' C / P' <= u + (Rw - S) D, and below, w' (C - P' D) / P' <= u (the
-// ceilings drop out against the integer u); the largest such w' is one
+// even-block move, row_begin_raw(S + w') <= u reads, with c = row_cost(u),
+// for w' >= Rw - S, w' C / P' <= c + (Rw - S) D, and below,
+// w' (C - P' D) / P' <= c (the ceilings drop out against the integer c, and
+// row_unit_at(a) <= u exactly when a <= c); the largest such w' is one
 // division.  The move adds at most one unit, so the owner is that estimate
 // or the workgroup before it.
 __host__ __device__ inline int row_owner(const DecodeSplit& d, uint32_t u) {
   const uint32_t Pp = (uint32_t)(d.P - d.S);
   const uint32_t Rp = (uint32_t)(d.Rw - d.S);
-  uint32_t wp = fdiv((u + Rp * (uint32_t)d.D) * Pp, d.by_c);
-  if (wp < Rp) wp = fdiv(u * Pp, d.by_cd);
+  const uint32_t c = row_cost(d, u);
+  uint32_t wp = fdiv((c + Rp * (uint32_t)d.D) * Pp, d.by_c);
+  if (wp < Rp) wp = fdiv(c * Pp, d.by_cd);
   int w = d.S + (int)(wp < Pp - 1 ? wp : Pp - 1);
   if (w > d.S && row_begin(d, w) > u) --w;
   return w;
@@ -166,14 +187,24 @@ inline DecodeSplit with_divisors(DecodeSplit d) {
   d.by_rw = make_fastdiv(d.Rw > 0 ? (uint32_t)d.Rw : 1u);
   d.by_ru = make_fastdiv(RU > 0 ? RU : 1u);
   d.by_c = make_fastdiv(d.C > 0 ? (uint32_t)d.C : 1u);
+  d.by_kbx = make_fastdiv((uint32_t)(d.KB + d.X));
   const long long cd = (long long)d.C - (long long)(d.P - d.S) * d.D;
   d.by_cd = make_fastdiv(cd > 0 ? (uint32_t)cd : 1u);
   return d;
 }
 
-// The split for P_max = slots workgroups.  Host only.
-inline DecodeSplit make_split_plain(int KB, int RB, int NB, int slots) {
+// What a run's crossing of a row band boundary costs on the cost axis: about
+// what a stream covers in the time of the arrival and the next band's start
+// (measured: 10 units), at most a quarter of a workgroup's share, so that
+// no run's window can fall into a gap whole.
+constexpr int kBoundaryCost = 10;
+constexpr int kBoundaryShare = 4;
+
+// The split for P_max = slots workgroups, before the band boundaries are
+// given a cost.  Host only.
+inline DecodeSplit make_split_flat(int KB, int RB, int NB, int slots) {
   DecodeSplit d;
+  d.X = 0;
   d.KB = KB;
   d.RB = RB;
   d.NB = NB;
@@ -221,6 +252,19 @@ inline DecodeSplit make_split_plain(int KB, int RB, int NB, int slots) {
     d.D = 0;
     d.C = (int)WU;
   }
+  return d;
+}
+
+// The split with the band boundaries' cost.  Host only.
+inline DecodeSplit make_split_plain(int KB, int RB, int NB, int slots) {
+  DecodeSplit d = make_split_flat(KB, RB, NB, slots);
+  const int Pp = d.P - d.S;
+  const long long share = Pp > 0 ? (long long)d.C / Pp : 0;
+  // (runs of a few units, a few microseconds in all, gain nothing from it:
+  // measured slower with X = 1 at 4 units per run)
+  const long long X = share >= 4 * kBoundaryShare ? share / kBoundaryShare : 0;
+  d.X = (int)(X < kBoundaryCost ? X : kBoundaryCost);
+  d.C += d.X * (NB - 1);
   return d;
 }
 
