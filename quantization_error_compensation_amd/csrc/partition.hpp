@@ -171,14 +171,17 @@ __host__ __device__ inline int rank_slot(const DecodeSplit& d, int w, int rb) {
 }
 __host__ __device__ inline int split_slots(const DecodeSplit& d) { return 4 * d.P; }
 
-// The planner's constants: rank units per rank workgroup (four bursts; the
-// last arriver of a rank band sums one partial per rank workgroup), and what
-// a rank workgroup's share of the projection stands for in row units: 2.5
-// per rank unit (16 KB of A against 8 KB of codes, plus x) and a fixed 4 for
-// its hand-off of the partial projection.
+// The planner's constants: rank units per rank workgroup (four bursts;
+// workgroup 0 sums one partial per rank workgroup), and what a rank
+// workgroup's share of the projection stands for in row units: 1.5 per rank
+// unit (16 KB of A against 8 KB of codes, but the rank stream starts at once
+// and its loads are wide rows).  Measured on the 28672 x 8192 layer at rank
+// 64: 2.5 per unit plus 4 for the hand-off left the rank workgroups' row
+// runs ending 5 us before the others; 1.5 gave the shortest call (1 and 2
+// measured longer).
 constexpr int kRankUnitsPerWg = 8;
-constexpr int kRankUnitCost2 = 5;   // twice the row-unit equivalents of one rank unit
-constexpr int kRankFixedCost = 4;
+constexpr int kRankUnitCost2 = 3;   // twice the row-unit equivalents of one rank unit
+constexpr int kRankFixedCost = 0;
 
 inline DecodeSplit with_divisors(DecodeSplit d) {
   const uint32_t RU = split_ru(d);
