@@ -22,9 +22,11 @@
 //            tokens hit 16 different bank groups;
 //   W stage  256 rows x 64 B of packed codes, piece p of row n at
 //            p ^ ((n >> 2) & 3) for the same reason;
-//   metadata per block: the 4-byte words holding each row's fp16 scale and
-//            zero-point nibble, and the block sums of x of each token (as
-//            three bf16 parts).
+//   sums     the block sums of x of each token (as three bf16 parts);
+// and, outside the ring, two slots of group metadata for 8 blocks at a time
+// (each row's fp16 scales and its zero-point word), loaded with the first
+// block of each 8: one lane per row and block cost 64 cache lines per load
+// instruction, once per block, which held the loads back.
 // A lane's weight operand for K step s is word 8*(lane/32) + s of its row,
 // converted to 128 + c in natural column order; the matching activations are
 // 16-byte piece 8*(lane/32) + s of its token.  Group-wise scales: each
@@ -62,21 +64,30 @@ struct PrefillParams {
 
 constexpr int kXStage = kPrefillBM * 256;  // 32 KB
 constexpr int kWStage = kPrefillBN * 64;   // 16 KB
-// metadata: scale words [256], zero-point words [256], sums of x [128][8 B],
-// and a spare area that keeps every wave's load count equal
-constexpr int kMScale = 0, kMZero = 1024, kMSum = 2048, kMSpare = 3072;
-constexpr int kMStage = kMSpare + 256;
-constexpr int kStage = kXStage + kWStage + kMStage;
+constexpr int kSStage = kPrefillBM * 8;    // block sums of x [128 tokens][8 B]
+constexpr int kStage = kXStage + kWStage + kSStage;
 constexpr int kStages = 3;
-static_assert(kStages * kStage <= 160 * 1024, "LDS ring exceeds 160 KB");
-// Loads into LDS each wave issues per block: 4 x, 2 W, 2 metadata.
-constexpr int kLoadsPerBlock = 8;
+// Group metadata by chunks of 8 blocks (one zero-point word's groups), two
+// chunk slots after the ring: per row the 5 dwords from the even scale at or
+// below its first (rows laid end to end, 20 dword loads of 64 lanes), then
+// the zero-point word of each row.
+constexpr int kChunkScales = kPrefillBN * 5 * 4;  // 5 KB
+constexpr int kChunk = kChunkScales + kPrefillBN * 4;
+constexpr int kChunkBase = kStages * kStage;
+static_assert(kChunkBase + 2 * kChunk <= 160 * 1024, "LDS exceeds 160 KB");
+// Loads into LDS each wave issues per block: 4 x, 2 W and, with group
+// scales, a quarter of the block sums (waves w and w + 4 load the same
+// quarter, so every wave's count is the same); per chunk of 8 blocks, 3 more
+// (scales or zero-point words), issued first.
+template <bool GROUPED>
+constexpr int kLoadsPerBlock = GROUPED ? 7 : 6;
+constexpr int kChunkLoadsPerWave = 3;
 static_assert(kPrefillWaves == 8 && kPrefillBN == 256 && kPrefillBM == 128, "tile shape");
 
 template <bool GROUPED>
 __global__ __launch_bounds__(512, 1) void prefill_kernel(PrefillParams p) {
   warm_kernel_args<sizeof(PrefillParams)>();
-  __shared__ __attribute__((aligned(16))) uint8_t smem[kStages * kStage];
+  __shared__ __attribute__((aligned(16))) uint8_t smem[kChunkBase + 2 * kChunk];
   __shared__ int s_last;
 
   const int tid = threadIdx.x;
@@ -101,9 +112,8 @@ __global__ __launch_bounds__(512, 1) void prefill_kernel(PrefillParams p) {
   // Buffer views of this tile; rows past T or N read as zero.
   const u32x4 xr = sdesc(p.x + (size_t)m0 * p.K, (uint32_t)rows_m * p.K * 2);
   const u32x4 wr = sdesc(p.wq + (size_t)n0 * (p.K / 8), (uint32_t)rows_n * (p.K / 2));
-  // Scale words: a 4-byte aligned word around each 2-byte scale.  N is a
-  // multiple of 16, so rows_n * G * 2 is a multiple of 4 and the word never
-  // reaches past the tile's last scale.
+  // Scales of the tile (n0 G is even, so the view starts on a dword; reads
+  // past the tile's rows give zeros).
   const u32x4 sr = sdesc(p.scales + (size_t)n0 * p.G, (uint32_t)rows_n * p.G * 2);
   // Without zero-points the view is empty: its loads read zero words.
   const u32x4 zr = p.has_z ? sdesc(p.zeros + (size_t)n0 * p.ZW, (uint32_t)rows_n * p.ZW * 4)
@@ -111,7 +121,25 @@ __global__ __launch_bounds__(512, 1) void prefill_kernel(PrefillParams p) {
   const u32x4 gr = sdesc(p.sblk, (uint32_t)KB * p.Tp * 8);
   const uint32_t lds0 = lds_addr(smem);
 
-  auto issue = [&](int kb, int stage) {
+  // The loads of block kb into a stage; with `chunk`, first the group
+  // metadata of the chunk kb / 8 into its slot.
+  auto issue = [&](int kb, int stage, bool chunk) {
+    if constexpr (GROUPED) {
+      if (chunk) {  // uniform: every wave issues 3 loads
+        const uint32_t C = lds0 + kChunkBase + ((kb >> 3) & 1) * kChunk;
+        for (int k = 0; k < kChunkLoadsPerWave; ++k) {
+          const int i = kChunkLoadsPerWave * wave + k;  // 0 .. 23
+          if (i < 20) {  // scales: dword f of rows laid end to end
+            const int f = 64 * i + lane, n = f / 5, d = f - 5 * n;
+            const uint32_t e0 = (uint32_t)(n * p.G + (kb & ~7)) & ~1u;
+            dma4(sr, C + 256 * i, e0 * 2 + 4 * (uint32_t)d);
+          } else {  // zero-point words of rows 64 (i - 20) + lane
+            const int n = 64 * (i - 20) + lane;
+            dma4(zr, C + kChunkScales + 256 * (i - 20), (uint32_t)(n * p.ZW + (kb >> 3)) * 4);
+          }
+        }
+      }
+    }
     const uint32_t S = lds0 + stage * kStage;
     for (int j = 0; j < 4; ++j) {  // x: tokens 16 wave + 4 j .. + 3
       const int t = 16 * wave + 4 * j + (lane >> 4);
@@ -125,19 +153,12 @@ __global__ __launch_bounds__(512, 1) void prefill_kernel(PrefillParams p) {
       dma16(wr, S + kXStage + (32 * wave + 16 * j) * 64,
             (uint32_t)n * (p.K / 2) + gp * 16 + (uint32_t)kb * 64);
     }
-    // Metadata, two 4-byte loads per wave with no branch (the same count in
-    // every wave): waves 0-3 the scale and zero-point words of rows
-    // 64 w + lane; waves 4-7 a quarter each of the sums of x of the tile's
-    // 128 tokens, plus a load into a spare area.
-    const uint32_t M = S + kXStage + kWStage;
-    const bool low = wave < 4;
-    const int j = wave & 3, n = 64 * j + lane;
-    dma4(low ? sr : gr, M + (low ? kMScale : kMSum) + 256 * j,
-         low ? ((uint32_t)((n * p.G + kb) * 2) & ~3u)
-             : (uint32_t)(kb * p.Tp + m0) * 8 + 256 * j + 4 * lane);
-    dma4(low ? zr : sr, M + (low ? kMZero + 256 * j : kMSpare),
-         low ? (uint32_t)(n * p.ZW + (kb >> 3)) * 4 : 0u);
+    if constexpr (GROUPED) {  // block sums of x, a quarter per wave (w and w + 4 alike)
+      const int j = wave & 3;
+      dma4(gr, S + kXStage + kWStage + 256 * j, (uint32_t)(kb * p.Tp + m0) * 8 + 256 * j + 4 * lane);
+    }
   };
+
 
   f32x16 acc[2][2];
   f32x16 tot[2][2];
@@ -179,9 +200,10 @@ __global__ __launch_bounds__(512, 1) void prefill_kernel(PrefillParams p) {
   };
 
   // K loop over the 3-stage ring.  At the top of iteration kb this wave's
-  // loads of blocks kb and kb + 1 are in flight (8 each); waiting until at
-  // most 8 remain completes block kb, and the barrier makes every wave's part
-  // of it visible.  Past the barrier every wave has finished reading block
+  // loads of blocks kb and kb + 1 are in flight (7 each with group scales,
+  // 6 without, after any chunk loads issued ahead of them); waiting until at
+  // most that many remain completes block kb (and the chunk loads of kb + 1),
+  // and the barrier makes every wave's part of it visible.  Past the barrier every wave has finished reading block
   // kb - 1, so its stage takes the loads of block kb + 2.  Past the last
   // block the loads repeat block kb1 - 1 into the free stage, which keeps the
   // count of loads in flight the same in every iteration.
@@ -195,25 +217,26 @@ __global__ __launch_bounds__(512, 1) void prefill_kernel(PrefillParams p) {
   // lanes of the upper half hold K = 8..15 of the offset step: zero there
   // (a mask, not a branch, so the reads stay ahead of their waits)
   const uint32_t qmask = q == 0 ? 0xFFFFFFFFu : 0u;
-  issue(kb0, 0);
-  issue(min(kb0 + 1, kb1 - 1), 1);
+  issue(kb0, 0, true);
+  issue(min(kb0 + 1, kb1 - 1), 1, kb0 + 1 < kb1 && ((kb0 + 1) & 7) == 0);
   u32x4 xc[2] = {u32x4{0u, 0u, 0u, 0u}, u32x4{0u, 0u, 0u, 0u}};  // carried: x of step 7
   uint32_t wc[2] = {0u, 0u};                                     // carried: code words of step 7
   float scc[2] = {0.f, 0.f};                                     // carried: scales
   for (int kb = kb0; kb < kb1; ++kb) {
     const int i = kb - kb0;
-    wait_vmcnt<kLoadsPerBlock>();
+    wait_vmcnt<kLoadsPerBlock<GROUPED>>();
     // lgkmcnt(0) through the builtin (0xC07F: vmcnt and expcnt at their
     // maxima), which the compiler's own wait insertion sees: the carried
     // step-7 operands then count as arrived.
     __builtin_amdgcn_s_waitcnt(0xC07F);
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
-    issue(min(kb + 2, kb1 - 1), (i + 2) % kStages);
+    issue(min(kb + 2, kb1 - 1), (i + 2) % kStages, kb + 2 < kb1 && ((kb + 2) & 7) == 0);
 
     const uint8_t* X = smem + (i % kStages) * kStage;
     const uint8_t* W = X + kXStage;
-    const uint8_t* M = W + kWStage;
+    const uint8_t* M = W + kWStage;  // block sums
+    const uint8_t* CH = smem + kChunkBase + ((kb >> 3) & 1) * kChunk;
     u32x4 wd[2][2];
     read_w(W, wd);
     float sc[2] = {0.f, 0.f};
@@ -223,17 +246,19 @@ __global__ __launch_bounds__(512, 1) void prefill_kernel(PrefillParams p) {
       // matrix-core step whose only non-zero terms are the three bf16 parts
       // of sum_x (token side) against the exact bf16 value -(128 + z) (row
       // side); then P gathers the eight code steps and is folded with s.
-      const uint32_t* Ms = reinterpret_cast<const uint32_t*>(M + kMScale);
-      const uint32_t* Mz = reinterpret_cast<const uint32_t*>(M + kMZero);
+      const uint32_t* Ms = reinterpret_cast<const uint32_t*>(CH);
+      const uint32_t* Mz = reinterpret_cast<const uint32_t*>(CH + kChunkScales);
       for (int ms = 0; ms < 2; ++ms) {
         const int t = wm * 64 + ms * 32 + i32;
-        const u32x2 sx = *reinterpret_cast<const u32x2*>(M + kMSum + t * 8);
+        const u32x2 sx = *reinterpret_cast<const u32x2*>(M + t * 8);
         xo[ms] = u32x4{sx.x & qmask, sx.y & qmask, 0u, 0u};
       }
       for (int ns = 0; ns < 2; ++ns) {
         const int n = wn * 64 + ns * 32 + i32;
-        const uint32_t sword = Ms[n];
-        const uint32_t sbits = (((n0 + n) * p.G + kb) & 1) ? (sword >> 16) : (sword & 0xFFFFu);
+        // scale of block kb: position (kb & 7) + (n G & 1) of the row's 5 dwords
+        const uint32_t pos = (uint32_t)(kb & 7) + ((uint32_t)(n * p.G) & 1u);
+        const uint32_t sword = Ms[5 * n + (pos >> 1)];
+        const uint32_t sbits = (pos & 1u) ? (sword >> 16) : (sword & 0xFFFFu);
         sc[ns] = half_bits_to_f32((uint16_t)sbits);
         // without zero-points the word reads as zero and z = 8 comes from
         // the xor (one path, so no branch splits the read from its wait)
