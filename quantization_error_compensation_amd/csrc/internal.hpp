@@ -14,7 +14,7 @@ constexpr int kBlockK = 128;          // K block: one scale group (g = 128) or a
 constexpr int kDecodeWaves = 8;                     // waves per decode workgroup, 16 rows each
 constexpr int kDecodeBandRows = 16 * kDecodeWaves;  // output rows per decode row band
 constexpr int kDecodeOccupancy = 1;                 // decode workgroups per compute unit
-constexpr int kProjTokens = 32;       // tokens per projection workgroup (prefill path)
+constexpr int kProjTokens = 64;       // tokens per projection workgroup (prefill path)
 constexpr int kPrefillBM = 128;       // tokens per prefill tile
 constexpr int kPrefillBN = 256;       // output rows per prefill tile
 constexpr int kPrefillWaves = 8;      // waves per prefill workgroup (2 x 4 of 64 x 64)

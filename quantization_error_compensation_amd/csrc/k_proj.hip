@@ -10,9 +10,9 @@
 // the prefill GEMM uses to remove the +128 offset of its integer-code
 // operands, and whole-row sums.
 //
-// projection_kernel: one workgroup per (32-token tile, K split); the four
-// waves take contiguous runs of 128-column blocks; the split's partial u (and
-// row sum) goes to the workspace.  finish_kernel: one thread per (token, j)
+// projection_kernel: one workgroup per (64-token tile, K split), each wave
+// 16 of the tokens against every rank; the split's partial u (and row sum)
+// goes to the workspace.  finish_kernel: one thread per (token, j)
 // sums the split partials in split order (deterministic), applies the gate
 // and writes alpha * v in fp32 and as a bf16 high/low pair.  With the
 // bottleneck-MLP gate (SPEAR summary, section 2.1 A), which needs every rank
@@ -45,12 +45,24 @@ struct ProjParams {
   int T, K, r, Tp, splits;
 };
 
+// The x tile (kProjTokens tokens) and all r rows of A for one 128-column
+// block go to LDS by direct buffer-to-LDS loads, 16 consecutive lanes
+// reading one 256-byte row (a load whose consecutive lanes read different
+// rows costs the address unit a cache-line lookup per lane group); 16-byte
+// piece e of row t sits at position e ^ (t % 16), so the fragment reads (one
+// lane per row) spread over the banks.  Two stages: the next block's loads
+// are issued after the barrier that retires the stage, before this block is
+// multiplied.  Wave w takes tokens 16 w .. + 15 of the tile against every
+// rank, and their block sums (a product with a tile of ones).
 template <int RTX>  // RTX = r / 16 rank tiles
-__global__ __launch_bounds__(256, 2) void projection_kernel(ProjParams p) {
+__global__ __launch_bounds__(256, 1) void projection_kernel(ProjParams p) {
   warm_kernel_args<sizeof(ProjParams)>();
-  constexpr int MT = 2;                  // 32 tokens = two 16-row MFMA tiles
+  static_assert(kProjTokens == 64, "four waves of 16 tokens");
+  constexpr int XB = kProjTokens * 256;  // x stage bytes
+  constexpr int AB = 16 * RTX * 256;     // A stage bytes
+  constexpr int SB = XB + AB;
   constexpr int RA = RTX > 0 ? RTX : 1;  // array extent (rank 0 still sums x)
-  __shared__ float red[4][MT][RTX + 1][4][64];
+  __shared__ __attribute__((aligned(16))) uint8_t smem[2 * SB];
 
   const int lane = threadIdx.x & 63, wave = wave_id();
   const int q = lane >> 4, c16 = lane & 15;
@@ -58,78 +70,94 @@ __global__ __launch_bounds__(256, 2) void projection_kernel(ProjParams p) {
   const int KB = p.K / kBlockK;
   const int kb0 = (int)((long long)KB * split / p.splits);
   const int kb1 = (int)((long long)KB * (split + 1) / p.splits);
-  const int nb = kb1 - kb0;
-  const int wb0 = kb0 + nb * wave / 4, wb1 = kb0 + nb * (wave + 1) / 4;
   const int t0 = tile * kProjTokens;
+  const int rows_t = min(kProjTokens, p.T - t0);
+  // views: token rows past T and rank rows past r read as zero
+  const u32x4 xr = sdesc(p.x + (size_t)t0 * p.K, (uint32_t)rows_t * p.K * 2);
+  const u32x4 ar = sdesc(p.A, (uint32_t)p.r * p.K * 2);
+  const uint32_t lds0 = lds_addr(smem);
 
-  const uint16_t* xr[MT];
-  for (int mt = 0; mt < MT; ++mt)  // clamped: rows past T are computed but never stored
-    xr[mt] = p.x + (size_t)min(t0 + 16 * mt + c16, p.T - 1) * p.K + 32 * q;
-  const uint16_t* ar[RA];
-  for (int rt = 0; rt < RTX; ++rt) ar[rt] = p.A + (size_t)(16 * rt + c16) * p.K + 32 * q;
+  // Loads per wave and block: 4 of x (4 tokens x 256 B each) and RTX of A.
+  auto issue = [&](int kb, int stage) {
+    const uint32_t S = lds0 + stage * SB;
+    for (int j = 0; j < 4; ++j) {
+      const int g = 4 * wave + j, t = 4 * g + (lane >> 4);
+      const uint32_t e = (uint32_t)((lane & 15) ^ (t & 15));
+      dma16(xr, S + g * 1024, (uint32_t)t * p.K * 2 + e * 16 + (uint32_t)kb * 256);
+    }
+    for (int k = 0; k < RTX; ++k) {
+      const int g = RTX * wave + k, row = 4 * g + (lane >> 4);
+      const uint32_t e = (uint32_t)((lane & 15) ^ (row & 15));
+      dma16(ar, S + XB + g * 1024, (uint32_t)row * p.K * 2 + e * 16 + (uint32_t)kb * 256);
+    }
+  };
 
-  f32x4 u[MT][RA];
-  f32x4 ssum[MT];
-  for (int mt = 0; mt < MT; ++mt) {
-    ssum[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
-    for (int rt = 0; rt < RTX; ++rt) u[mt][rt] = f32x4{0.f, 0.f, 0.f, 0.f};
-  }
+  f32x4 u[RA];
+  f32x4 ssum = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int rt = 0; rt < RTX; ++rt) u[rt] = f32x4{0.f, 0.f, 0.f, 0.f};
   const u32x4 ones = {kBf16One, kBf16One, kBf16One, kBf16One};
+  const int tl = 16 * wave + c16;  // this lane's token row in the tile
 
-  for (int blk = wb0; blk < wb1; ++blk) {
-    u32x4 xf[MT][4], af[RA][4];
-    for (int mt = 0; mt < MT; ++mt)
-      for (int i = 0; i < 4; ++i) xf[mt][i] = load16(xr[mt] + (size_t)blk * kBlockK + 8 * i);
-    for (int rt = 0; rt < RTX; ++rt)
-      for (int i = 0; i < 4; ++i) af[rt][i] = load16(ar[rt] + (size_t)blk * kBlockK + 8 * i);
-    for (int mt = 0; mt < MT; ++mt) {
-      f32x4 sb = mfma16x16x32(xf[mt][0], ones, f32x4{0.f, 0.f, 0.f, 0.f});
-      for (int i = 1; i < 4; ++i) sb = mfma16x16x32(xf[mt][i], ones, sb);
-      for (int rt = 0; rt < RTX; ++rt)
-        for (int i = 0; i < 4; ++i) u[mt][rt] = mfma16x16x32(xf[mt][i], af[rt][i], u[mt][rt]);
-      ssum[mt] += sb;
-      // every column of the ones-product holds the row sum; column 0 stores
-      // it as three bf16 parts hi + mid + lo that add up to the fp32 sum
-      // exactly (the prefill GEMM feeds them to the matrix cores)
+  issue(kb0, 0);
+  for (int kb = kb0; kb < kb1; ++kb) {
+    const int i = kb - kb0;
+    // this block's loads are done (the two block-sum stores of the previous
+    // block, issued after them, may still be in flight), then every wave's
+    // are, and every wave is done with the other stage
+    if (i == 0) wait_vmcnt<0>();
+    else wait_vmcnt<2>();
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    if (kb + 1 < kb1) issue(kb + 1, (i + 1) & 1);
+    const uint8_t* X = smem + (i & 1) * SB;
+    const uint8_t* Am = X + XB;
+    f32x4 sb = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {  // K step s: piece 4 s + q of each row
+      const int pc = 4 * s + q;
+      const u32x4 xf = *reinterpret_cast<const u32x4*>(X + tl * 256 + ((pc ^ (tl & 15)) * 16));
+      sb = mfma16x16x32(xf, ones, sb);
+      for (int rt = 0; rt < RTX; ++rt) {
+        const int j = 16 * rt + c16;
+        const u32x4 af = *reinterpret_cast<const u32x4*>(Am + j * 256 + ((pc ^ (j & 15)) * 16));
+        u[rt] = mfma16x16x32(xf, af, u[rt]);
+      }
+    }
+    ssum += sb;
+    // every column of the ones-product holds the row sum; column 0 stores
+    // it as three bf16 parts hi + mid + lo that add up to the fp32 sum
+    // exactly (the prefill GEMM feeds them to the matrix cores).  Two
+    // stores per block in every wave (lanes of other columns masked).
+    {
+      const int t = t0 + 16 * wave + 4 * q;
+      u32x4 tw[2];
+      for (int v = 0; v < 4; ++v) {
+        const float sv = t + v < p.T ? sb[v] : 0.f;
+        const uint32_t hi = f32_to_bf16_rne(sv);
+        const float r1 = sv - __uint_as_float(hi << 16);
+        const uint32_t mid = f32_to_bf16_rne(r1);
+        const uint32_t lo = f32_to_bf16_rne(r1 - __uint_as_float(mid << 16));
+        tw[v >> 1][2 * (v & 1)] = hi | (mid << 16);
+        tw[v >> 1][2 * (v & 1) + 1] = lo;
+      }
       if (c16 == 0) {
-        const int t = t0 + 16 * mt + 4 * q;
-        u32x4 tw[2];
-        for (int v = 0; v < 4; ++v) {
-          const float sv = t + v < p.T ? sb[v] : 0.f;
-          const uint32_t hi = f32_to_bf16_rne(sv);
-          const float r1 = sv - __uint_as_float(hi << 16);
-          const uint32_t mid = f32_to_bf16_rne(r1);
-          const uint32_t lo = f32_to_bf16_rne(r1 - __uint_as_float(mid << 16));
-          tw[v >> 1][2 * (v & 1)] = hi | (mid << 16);
-          tw[v >> 1][2 * (v & 1) + 1] = lo;
-        }
-        uint32_t* dst = p.sblk + ((size_t)blk * p.Tp + t) * 2;
+        uint32_t* dst = p.sblk + ((size_t)kb * p.Tp + t) * 2;
         *reinterpret_cast<u32x4*>(dst) = tw[0];
         *reinterpret_cast<u32x4*>(dst + 4) = tw[1];
       }
     }
   }
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
-  // In-workgroup reduction over the four waves (fixed order).
-  for (int mt = 0; mt < MT; ++mt) {
-    for (int rt = 0; rt < RTX; ++rt)
-      for (int v = 0; v < 4; ++v) red[wave][mt][rt][v][lane] = u[mt][rt][v];
-    for (int v = 0; v < 4; ++v) red[wave][mt][RTX][v][lane] = ssum[mt][v];
-  }
-  __syncthreads();
-  constexpr int kElems = MT * (RTX + 1) * 4 * 64;
+  // This split's partial u (and row sums): lane holds tokens 4 q + v of the
+  // wave's 16 against rank 16 rt + c16.
   const int R1 = p.r + 1;
-  for (int e = threadIdx.x; e < kElems; e += 256) {
-    const int l = e & 63, v = (e >> 6) & 3, rt = (e >> 8) % (RTX + 1), mt = (e >> 8) / (RTX + 1);
-    const float s = red[0][mt][rt][v][l] + red[1][mt][rt][v][l] + red[2][mt][rt][v][l] +
-                    red[3][mt][rt][v][l];
-    const int t = t0 + 16 * mt + 4 * (l >> 4) + v;
+  for (int v = 0; v < 4; ++v) {
+    const int t = t0 + 16 * wave + 4 * q + v;
     if (t >= p.T) continue;
-    if (rt < RTX) {
-      p.upart[((size_t)split * p.T + t) * R1 + 16 * rt + (l & 15)] = s;
-    } else if ((l & 15) == 0) {
-      p.upart[((size_t)split * p.T + t) * R1 + p.r] = s;
-    }
+    float* dst = p.upart + ((size_t)split * p.T + t) * R1;
+    for (int rt = 0; rt < RTX; ++rt) dst[16 * rt + c16] = u[rt][v];
+    if (c16 == 0) dst[p.r] = ssum[v];
   }
 }
 
