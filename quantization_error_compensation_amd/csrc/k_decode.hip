@@ -26,9 +26,8 @@
 //     burst computes;
 //   * x of the burst is loaded once per workgroup (4 tokens x 256 B per
 //     instruction, full cache lines, spread over the waves), permuted into
-//     the matrix-core K order and written to a double-buffered LDS area with
-//     the block sums of x (vector adds and a 16-lane DPP tree); one barrier
-//     per burst publishes both to all waves;
+//     the matrix-core K order and written to a double-buffered LDS area; one
+//     barrier per burst publishes it to all waves;
 //   * codes: 16 bytes per lane per block, four consecutive lanes reading a
 //     row's 64 contiguous bytes (16 rows x 64 B per instruction: lanes that
 //     read 16 different rows slowed the address unit), turned into the
@@ -37,7 +36,10 @@
 //   * group scale and zero-point word of the lane's row: one small load each
 //     per block, straight into registers;
 //   * matrix cores 16x16x32: tokens (padded to 16 or 32) x 16 rows x 32 K;
-//     the block sums remove the 128 + z offset in fp32.
+//     each K step also multiplies x by the exact bf16 -(128 + z), which
+//     removes the codes' offset inside the same fp32 chain (block sums of x
+//     in vector code cost more than these matrix-core steps: the decode
+//     kernel's vector units, not its matrix cores, are the busy ones).
 // In a rank segment the waves form W / 4 phases of four 16-rank tiles; phase
 // f takes block f of each burst and the phases are summed in LDS at the end.
 // The band finisher adds alpha * B * v as a small K = r matrix-core product
@@ -104,16 +106,15 @@ constexpr int XROW = 272;            // LDS row of one token: 256 B + 16 B pad
 constexpr int kSpinLimit = 1 << 20;
 
 // Blocks per burst: 4 in row segments up to 16 tokens (2 above, for
-// registers), one per phase in rank segments.  One
-// x buffer holds [kMax][16 MT tokens][XROW] of x, then the block sums of x
-// [kMax][16 MT] fp32.
+// registers), one per phase in rank segments.  One x buffer holds
+// [kMax][16 MT tokens][XROW] of x, then [kMax][16 MT] floats of room that the
+// MLP gate's working area and the rank phase sums also use.
 template <int MT>
 struct Burst {
   static constexpr int kRow = MT == 1 ? 4 : 2;
   static constexpr int kRank = PH;
   static constexpr int kMax = kRow > kRank ? kRow : kRank;
-  static constexpr int kSums = kMax * 16 * MT * XROW;  // byte offset of the block sums
-  static constexpr int kBuf = kSums + kMax * 16 * MT * 4;  // bytes of one x buffer
+  static constexpr int kBuf = kMax * 16 * MT * (XROW + 4);  // bytes of one x buffer
 };
 
 // ------------------------------------------------------------- x staging
@@ -152,40 +153,18 @@ __device__ __forceinline__ void x_issue(const DecodeParams& p, int wave, int lan
   }
 }
 
-// Sum of a float over the 16 lanes of a row (every lane gets the total).
-template <int CTRL>
-__device__ __forceinline__ float dpp_f32(float x) {
-  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
-}
-__device__ __forceinline__ float row16_sum(float v) {
-  v += dpp_f32<0xB1>(v);   // quad_perm 1,0,3,2
-  v += dpp_f32<0x4E>(v);   // quad_perm 2,3,0,1
-  v += dpp_f32<0x141>(v);  // row_half_mirror
-  v += dpp_f32<0x140>(v);  // row_mirror
-  return v;
-}
-
-// Store the burst's x into buf; with SUMS, also the sum of each token's 128
-// values of each block (fp32: each lane adds its 8 values in order, then the
-// 16 lanes of the token's row are added as a tree).
-template <int MT, int NS, bool SUMS>
+// Store the burst's x into buf, each 16-byte piece in the matrix-core K
+// order.
+template <int MT, int NS>
 __device__ __forceinline__ void x_store(uint8_t* buf, int wave, int lane,
                                         const XStage<MT, NS>& s) {
   using S = XStage<MT, NS>;
-  float* sums = reinterpret_cast<float*>(buf + Burst<MT>::kSums);
   for (int k = 0; k < S::kLoads; ++k) {
     const int e = k * W + wave, i = e / (4 * MT);
     const int t = 4 * (e % (4 * MT)) + (lane >> 4);
-    if (S::kPieces % W == 0 || e < S::kPieces) {
+    if (S::kPieces % W == 0 || e < S::kPieces)
       *reinterpret_cast<u32x4*>(buf + (i * 16 * MT + t) * XROW + 16 * (lane & 15)) =
           x_permute8(s.g[k]);
-      if constexpr (SUMS) {
-        float a = 0.f;
-        for (int j = 0; j < 4; ++j) a += bf16_lo(s.g[k][j]) + bf16_hi(s.g[k][j]);
-        a = row16_sum(a);
-        if ((lane & 15) == 0) sums[i * 16 * MT + t] = a;
-      }
-    }
   }
 }
 
@@ -290,7 +269,7 @@ __device__ void rank_segment(const DecodeParams& p, int rb, int lo, int hi, uint
   auto consume = [&](RankStage<MT, NS>& s, int b) {
     uint8_t* buf = xlds + (burst & 1) * Burst<MT>::kBuf;
     ++burst;
-    x_store<MT, NS, false>(buf, wave, lane, s.x);
+    x_store<MT, NS>(buf, wave, lane, s.x);
     for (int j = 0; j < 4; ++j) {  // piece e of row r at position e ^ r
       const int r = (lane >> 4) + 4 * j;
       *reinterpret_cast<u32x4*>(cl + r * 256 + (((lane & 15) ^ r) * 16)) = s.a[j];
@@ -348,15 +327,22 @@ struct Meta {
   static_assert(kChunk <= 64, "an entry per lane");
 };
 
-// The packed word of one (row, block): scale bits s, zero-point word zw of
-// the block's group of eight (none: z = 8).
+// The packed word of one (row, block): fp16 scale bits s in the low half and
+// the bf16 bits of -(128 + z) (exact) in the high half, z from the
+// zero-point word zw of the block's group of eight (none: z = 8).
 __device__ __forceinline__ uint32_t meta_pack(uint32_t s, uint32_t zw, int blk, bool has_z) {
   const uint32_t z = has_z ? (zw >> (4 * (blk & 7))) & 15u : 8u;
-  return (s & 0xFFFFu) | ((0xD800u | (z << 3)) << 16);  // fp16 of -(128 + z)
+  return (s & 0xFFFFu) | ((0xC300u | z) << 16);
+}
+// A matrix-core operand of eight copies of the bf16 value in the high half
+// of w (one K group of one row).
+__device__ __forceinline__ u32x4 bf16_splat_hi(uint32_t w) {
+  const uint32_t pair = (w & 0xFFFF0000u) | (w >> 16);
+  return u32x4{pair, pair, pair, pair};
 }
 
 // What one burst of a row segment takes from memory: x (permuted into LDS
-// with its block sums when the burst starts), the codes, and one row of the
+// when the burst starts), the codes, and one row of the
 // next metadata chunk.  Each burst's loads are issued one burst ahead, so
 // they are in flight while the previous burst computes; every load is
 // issued on every burst (out of range, with no memory access, past the
@@ -408,10 +394,19 @@ __device__ void row_segment(const DecodeParams& p, int band, int lo, int hi, uin
 
   // acc: the grouped result; per-channel: one product accumulator per block
   // of a burst (accb), summed at the end
-  f32x4 acc[MT], ssum[MT], accb[NS][MT];
+  f32x4 acc[MT], accb[NS][MT];
   for (int mt = 0; mt < MT; ++mt) {
-    acc[mt] = ssum[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    acc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
     for (int i = 0; i < NS; ++i) accb[i][mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+  // Per-channel: the row's -(128 + z) operand and scale, read before the loop.
+  u32x4 nzrow = u32x4{0u, 0u, 0u, 0u};
+  float scrow = 0.f;
+  if constexpr (!GROUPED) {
+    const int n = rc + c16;
+    const uint32_t z = p.has_z ? p.zeros[(size_t)n * p.ZW] & 15u : 8u;
+    nzrow = bf16_splat_hi((0xC300u | z) << 16);
+    scrow = half_bits_to_f32(p.scales[n]);
   }
 
   auto issue = [&](RowStage<MT, NS>& s, int b) {
@@ -430,9 +425,8 @@ __device__ void row_segment(const DecodeParams& p, int band, int lo, int hi, uin
 
   auto consume = [&](RowStage<MT, NS>& s, int b) {
     uint8_t* buf = xlds + (burst & 1) * Burst<MT>::kBuf;
-    const float* sums = reinterpret_cast<const float*>(buf + Burst<MT>::kSums);
     ++burst;
-    x_store<MT, NS, true>(buf, wave, lane, s.x);
+    x_store<MT, NS>(buf, wave, lane, s.x);
     for (int i = 0; i < NS; ++i)
       *reinterpret_cast<u32x4*>(cl + i * 1024 + lr * 64 + ((lj ^ code_swz(lr)) * 16)) = s.w[i];
     lds_barrier();
@@ -447,16 +441,18 @@ __device__ void row_segment(const DecodeParams& p, int band, int lo, int hi, uin
         for (int i = 0; i < NS; ++i) meta[i] = m[i];
       }
     }
-    // Both blocks' operands first, then their matrix-core chains interleaved
-    // (two independent chains hide each other's latency), then the per-block
-    // scale fold.  A block past the segment has x = 0: it adds nothing.
-    u32x4 xf[NS][MT][4], wb[NS][4];
-    f32x4 sb[NS][MT];  // block sums of this lane's four tokens
+    // All blocks' operands first, then their matrix-core chains interleaved
+    // (independent chains hide each other's latency), then the per-block
+    // scale fold.  The +128 offset of the code operands comes out in the
+    // matrix cores too: each K step also multiplies x by -(128 + z) (exact
+    // in bf16), so a chain sums (c - z) x directly.  A block past the
+    // segment has x = 0: it adds nothing.
+    u32x4 xf[NS][MT][4], wb[NS][4], nzb[NS];
 #pragma unroll
     for (int i = 0; i < NS; ++i) {
       x_frags<MT>(buf, i, lane, xf[i]);
-      for (int mt = 0; mt < MT; ++mt)
-        sb[i][mt] = *reinterpret_cast<const f32x4*>(sums + i * 16 * MT + 16 * mt + 4 * q);
+      if constexpr (GROUPED) nzb[i] = bf16_splat_hi(meta[i]);
+      else nzb[i] = nzrow;
       const u32x4 cw =
           *reinterpret_cast<const u32x4*>(cl + i * 1024 + c16 * 64 + ((q ^ code_swz(c16)) * 16));
       wb[i][0] = codes_to_bf16_offset(cw.x);
@@ -469,24 +465,25 @@ __device__ void row_segment(const DecodeParams& p, int band, int lo, int hi, uin
 #pragma unroll
       for (int jj = 0; jj < 4; ++jj)
         for (int i = 0; i < NS; ++i)
-          for (int mt = 0; mt < MT; ++mt)
+          for (int mt = 0; mt < MT; ++mt) {
             P[i][mt] = mfma16x16x32(xf[i][mt][jj], wb[i][jj],
                                     jj == 0 ? f32x4{0.f, 0.f, 0.f, 0.f} : P[i][mt]);
+            P[i][mt] = mfma16x16x32(xf[i][mt][jj], nzb[i], P[i][mt]);
+          }
 #pragma unroll
       for (int i = 0; i < NS; ++i) {
         const float sc = half_bits_to_f32((uint16_t)meta[i]);
-        const float nz = half_bits_to_f32((uint16_t)(meta[i] >> 16));  // -(128 + z)
         for (int mt = 0; mt < MT; ++mt)
-          for (int v = 0; v < 4; ++v)
-            acc[mt][v] = fmaf(sc, fmaf(nz, sb[i][mt][v], P[i][mt][v]), acc[mt][v]);
+          for (int v = 0; v < 4; ++v) acc[mt][v] = fmaf(sc, P[i][mt][v], acc[mt][v]);
       }
     } else {
 #pragma unroll
       for (int jj = 0; jj < 4; ++jj)
         for (int i = 0; i < NS; ++i)
-          for (int mt = 0; mt < MT; ++mt) accb[i][mt] = mfma16x16x32(xf[i][mt][jj], wb[i][jj], accb[i][mt]);
-      for (int i = 0; i < NS; ++i)
-        for (int mt = 0; mt < MT; ++mt) ssum[mt] += sb[i][mt];
+          for (int mt = 0; mt < MT; ++mt) {
+            accb[i][mt] = mfma16x16x32(xf[i][mt][jj], wb[i][jj], accb[i][mt]);
+            accb[i][mt] = mfma16x16x32(xf[i][mt][jj], nzb[i], accb[i][mt]);
+          }
     }
     // Row k % 16 of the next chunk (read from burst 16 (j + 1) on).
     if constexpr (GROUPED)
@@ -519,15 +516,11 @@ __device__ void row_segment(const DecodeParams& p, int band, int lo, int hi, uin
   }
   pipeline2(lo, hi, NS, s0, s1, issue, consume);
 
-  if constexpr (!GROUPED) {  // per-channel: one scale and one offset correction per row
+  if constexpr (!GROUPED) {  // per-channel: one scale per row
     for (int mt = 0; mt < MT; ++mt)
       for (int i = 0; i < NS; ++i) acc[mt] += accb[i][mt];
-    const int n = rc + c16;
-    const float sc = half_bits_to_f32(p.scales[n]);
-    const int z = p.has_z ? (int)(p.zeros[(size_t)n * p.ZW] & 15u) : 8;
-    const float mz = -(float)(128 + z);
     for (int mt = 0; mt < MT; ++mt)
-      for (int v = 0; v < 4; ++v) acc[mt][v] = sc * fmaf(mz, ssum[mt][v], acc[mt][v]);
+      for (int v = 0; v < 4; ++v) acc[mt][v] = scrow * acc[mt][v];
   }
   for (int mt = 0; mt < MT; ++mt) yo[mt] = acc[mt];
 }
