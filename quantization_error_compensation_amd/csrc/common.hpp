@@ -164,7 +164,8 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
 // Lane i's 16 (or 4) bytes at desc + off land at LDS address lds + 16 i (or
 // 4 i); lds must be wave-uniform (it is read from the first lane).  The
 // whole offset is the per-lane one, so every byte is checked against the
-// descriptor's range (past it: zero).
+// descriptor's range (past it: zero).  The global address of a lane's load
+// is aligned to its size (16 or 4 bytes).
 __device__ __forceinline__ void dma16(u32x4 desc, uint32_t lds, uint32_t off) {
   uint32_t saved;
   asm volatile(
