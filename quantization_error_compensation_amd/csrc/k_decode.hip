@@ -23,7 +23,8 @@
 // x is read from L2 once per BR rows, and few loads queue per compute unit):
 //   * every load of a burst (x, codes or A rows, metadata) is issued one
 //     burst ahead, into registers, so it is in flight while the previous
-//     burst computes;
+//     burst computes (in row segments the second half of the waves issues
+//     it after the previous burst's barrier, the first half before);
 //   * x of the burst is loaded once per workgroup (4 tokens x 256 B per
 //     instruction, full cache lines, spread over the waves), permuted into
 //     the matrix-core K order and written to a double-buffered LDS area; one
@@ -187,6 +188,29 @@ __device__ __forceinline__ void x_frags(const uint8_t* buf, int i, int lane, u32
 // along a row) and the reads (one lane per row) over the banks.
 __device__ __forceinline__ int code_swz(int r) { return ((r >> 1) ^ (r >> 2)) & 3; }
 constexpr int kCodeArea = 4 * 1024;  // bytes per wave: up to four blocks
+
+// The same two stages, with each burst's loads issued inside the previous
+// burst's consume, right after its barrier and before its compute.  The
+// second half of a workgroup's waves runs its row segments this way.  The
+// two waves that share a SIMD compute a burst at the same time and the
+// first half gets the SIMD first (it finishes about 0.4 us earlier); a wave
+// of the second half then issued its next loads only after its compute,
+// where the queue at the memory pipeline held it 0.3-0.4 us on the way to
+// the next barrier.  Issued before its compute, that wait overlaps the first
+// half's compute; the loads have one compute phase to arrive instead of a
+// whole burst, which is enough for the second half's later use.
+template <class Stage, class Issue, class Consume>
+__device__ __forceinline__ void pipeline2_late(int lo, int hi, int ns, Stage& s0, Stage& s1,
+                                               Issue&& issue, Consume&& consume) {
+  const int nb = (hi - lo + ns - 1) / ns;
+  int b = lo;
+  for (int k = 0; k + 1 < nb; k += 2, b += 2 * ns) {
+    consume(s0, b, [&] { issue(s1, b + ns); });
+    consume(s1, b + ns, [&] { issue(s0, b + 2 * ns); });
+  }
+  if (nb & 1) consume(s0, b, [&] { issue(s1, b + ns); });
+  __builtin_amdgcn_s_waitcnt(0);
+}
 
 // ------------------------------------------------------------ rank segment
 // A barrier that leaves global loads in flight: only this wave's LDS writes
@@ -423,13 +447,20 @@ __device__ void row_segment(const DecodeParams& p, int band, int lo, int hi, uin
     }
   };
 
-  auto consume = [&](RowStage<MT, NS>& s, int b) {
+  // after(): the next burst's loads on the waves that issue them past the
+  // barrier (nothing on the others).  The scheduling barriers keep this
+  // burst's LDS stores from moving up into the previous burst's compute and
+  // the next burst's loads from moving past this one's start.
+  auto consume = [&](RowStage<MT, NS>& s, int b, auto&& after) {
+    __builtin_amdgcn_sched_barrier(0);
     uint8_t* buf = xlds + (burst & 1) * Burst<MT>::kBuf;
     ++burst;
     x_store<MT, NS>(buf, wave, lane, s.x);
     for (int i = 0; i < NS; ++i)
       *reinterpret_cast<u32x4*>(cl + i * 1024 + lr * 64 + ((lj ^ code_swz(lr)) * 16)) = s.w[i];
     lds_barrier();
+    after();
+    __builtin_amdgcn_sched_barrier(0);
     const int k = (b - lo) / NS, j = k / 16;  // this burst's chunk
     uint32_t meta[NS];  // packed words of blocks b .. b + NS - 1 for row c16
     if constexpr (GROUPED) {
@@ -514,7 +545,12 @@ __device__ void row_segment(const DecodeParams& p, int band, int lo, int hi, uin
     issue(s0, lo);
     mid();
   }
-  pipeline2(lo, hi, NS, s0, s1, issue, consume);
+  if (wave < W / 2) {
+    auto consume0 = [&](RowStage<MT, NS>& s, int b) { consume(s, b, [] {}); };
+    pipeline2(lo, hi, NS, s0, s1, issue, consume0);
+  } else {
+    pipeline2_late(lo, hi, NS, s0, s1, issue, consume);
+  }
 
   if constexpr (!GROUPED) {  // per-channel: one scale per row
     for (int mt = 0; mt < MT; ++mt)
