@@ -26,7 +26,8 @@
 //     burst computes (in row segments the second half of the waves issues
 //     it after the previous burst's barrier, the first half before);
 //   * x of the burst is loaded once per workgroup (4 tokens x 256 B per
-//     instruction, full cache lines, spread over the waves), permuted into
+//     instruction, full cache lines, spread over the waves: in row segments
+//     three per wave of the first half, one per wave of the second), permuted into
 //     the matrix-core K order and written to a double-buffered LDS area; one
 //     barrier per burst publishes it to all waves;
 //   * codes: 16 bytes per lane per block, four consecutive lanes reading a
@@ -60,6 +61,8 @@
 // units every wait ends.  The waits are bounded all the same: one that gives
 // up writes NaN (or publishes NaN) and sets an error bit
 // (spear_ec_workspace_status).
+#include <type_traits>
+
 #include "common.hpp"
 #include "internal.hpp"
 
@@ -121,8 +124,9 @@ struct Burst {
 // ------------------------------------------------------------- x staging
 // x of blocks [b, b + NS) into an LDS buffer [NS][16*MT tokens][XROW], each
 // 16-byte piece already in the matrix-core K order.  The burst is NS x 4MT
-// pieces of 4 tokens x 256 B; piece e = k W + w (block e / 4MT, tokens
-// 4 (e % 4MT) .. +3) is load k of wave w (lane: token + l/16, 16 B l%16).
+// pieces of 4 tokens x 256 B; in rank segments piece e = k W + w (block
+// e / 4MT, tokens 4 (e % 4MT) .. +3) is load k of wave w (lane: token +
+// l/16, 16 B l%16); row segments split the pieces unevenly (below).
 // Every wave issues the same loads whatever T is, so the count of loads in
 // flight, and with it every wait, is path-independent: lanes of tokens past
 // T, pieces past the burst, blocks past the segment and all lanes when live
@@ -166,6 +170,48 @@ __device__ __forceinline__ void x_store(uint8_t* buf, int wave, int lane,
     if (S::kPieces % W == 0 || e < S::kPieces)
       *reinterpret_cast<u32x4*>(buf + (i * 16 * MT + t) * XROW + 16 * (lane & 15)) =
           x_permute8(s.g[k]);
+  }
+}
+
+// Row segments split the burst's 16 x pieces unevenly: the first half of
+// the waves loads three each (pieces 4 j + wave), the second half one each
+// (piece 12 + wave - 4).  The second half's waves get the SIMD last in each
+// burst's compute; what they load and store before the next barrier is
+// what the whole workgroup waits for (measured at 16 tokens on the 28672 x
+// 8192 layer: 0.7 us less per call than two pieces each, and 0.5 us less at
+// one token on the 4096 and 8192 layers).
+template <int H>
+struct XRowSplit {
+  static constexpr int kLoads = H == 0 ? 3 : 1;
+};
+__device__ __forceinline__ int x_row_piece(int h, int j, int wave) {
+  return h == 0 ? 4 * j + wave : 12 + wave - W / 2;
+}
+template <int MT>
+struct XRowStage {
+  u32x4 g[3];
+};
+template <int MT, int NS, int H>
+__device__ __forceinline__ void x_issue_row(const DecodeParams& p, int wave, int lane, int b, int hi,
+                                            bool live, XRowStage<MT>& s) {
+  static_assert(W == 8 && NS * 4 * MT == 16, "16 pieces over 8 waves");
+  const uint32_t xrowB = (uint32_t)p.K * 2;
+  const rsrc_t xr = make_rsrc(p.x, (uint32_t)p.T * xrowB);
+  for (int j = 0; j < XRowSplit<H>::kLoads; ++j) {
+    const int e = x_row_piece(H, j, wave), i = e / (4 * MT);
+    const int t = 4 * (e % (4 * MT)) + (lane >> 4);
+    const bool ok = live && t < p.T && b + i < hi;
+    const uint32_t vo = ok ? (uint32_t)t * xrowB + 16u * (lane & 15) : 0x80000000u;
+    s.g[j] = bload16(xr, vo, __builtin_amdgcn_readfirstlane((uint32_t)min(b + i, hi - 1) * 256));
+  }
+}
+template <int MT, int NS, int H>
+__device__ __forceinline__ void x_store_row(uint8_t* buf, int wave, int lane, const XRowStage<MT>& s) {
+  for (int j = 0; j < XRowSplit<H>::kLoads; ++j) {
+    const int e = x_row_piece(H, j, wave), i = e / (4 * MT);
+    const int t = 4 * (e % (4 * MT)) + (lane >> 4);
+    *reinterpret_cast<u32x4*>(buf + (i * 16 * MT + t) * XROW + 16 * (lane & 15)) =
+        x_permute8(s.g[j]);
   }
 }
 
@@ -373,7 +419,7 @@ __device__ __forceinline__ u32x4 bf16_splat_hi(uint32_t w) {
 // segment), so the compiler's wait counts stay exact.
 template <int MT, int NS>
 struct RowStage {
-  XStage<MT, NS> x;
+  XRowStage<MT> x;
   u32x4 w[NS];
   uint32_t ms, mz;
 };
@@ -433,9 +479,9 @@ __device__ void row_segment(const DecodeParams& p, int band, int lo, int hi, uin
     scrow = half_bits_to_f32(p.scales[n]);
   }
 
-  auto issue = [&](RowStage<MT, NS>& s, int b) {
+  auto issue = [&](RowStage<MT, NS>& s, int b, auto half) {
     const bool live = b < hi;  // a burst past the segment loads nothing
-    x_issue<MT, NS>(p, wave, lane, b, hi, live, s.x);
+    x_issue_row<MT, NS, decltype(half)::value>(p, wave, lane, b, hi, live, s.x);
     const uint32_t wv = live ? wo : kOut;
     for (int i = 0; i < NS; ++i)
       s.w[i] = bload16(wr, wv, __builtin_amdgcn_readfirstlane((uint32_t)min(b + i, hi - 1) * 64));
@@ -451,11 +497,11 @@ __device__ void row_segment(const DecodeParams& p, int band, int lo, int hi, uin
   // barrier (nothing on the others).  The scheduling barriers keep this
   // burst's LDS stores from moving up into the previous burst's compute and
   // the next burst's loads from moving past this one's start.
-  auto consume = [&](RowStage<MT, NS>& s, int b, auto&& after) {
+  auto consume = [&](RowStage<MT, NS>& s, int b, auto&& after, auto half) {
     __builtin_amdgcn_sched_barrier(0);
     uint8_t* buf = xlds + (burst & 1) * Burst<MT>::kBuf;
     ++burst;
-    x_store<MT, NS>(buf, wave, lane, s.x);
+    x_store_row<MT, NS, decltype(half)::value>(buf, wave, lane, s.x);
     for (int i = 0; i < NS; ++i)
       *reinterpret_cast<u32x4*>(cl + i * 1024 + lr * 64 + ((lj ^ code_swz(lr)) * 16)) = s.w[i];
     lds_barrier();
@@ -533,23 +579,36 @@ __device__ void row_segment(const DecodeParams& p, int band, int lo, int hi, uin
   // would otherwise guard the loop's first register writes with a wait for
   // every load, on every burst.
   __builtin_amdgcn_s_waitcnt(0);
-  if constexpr (GROUPED) {
-    uint32_t m0s[16], m0z[16];  // row n, this lane's entry
-    const int blk = meta_blk(lo);
-    for (int n = 0; n < 16; ++n) m0s[n] = meta_scale(n, blk);
-    for (int n = 0; n < 16; ++n) m0z[n] = meta_zero(n, blk);
-    issue(s0, lo);
-    mid();
-    for (int n = 0; n < 16; ++n) *mp_at(0, n, ment) = meta_pack(m0s[n], m0z[n], blk, p.has_z);
-  } else {
-    issue(s0, lo);
-    mid();
-  }
+  auto run = [&](auto half, auto&& loop) {
+    auto iss = [&](RowStage<MT, NS>& s, int b) { issue(s, b, half); };
+    if constexpr (GROUPED) {
+      uint32_t m0s[16], m0z[16];  // row n, this lane's entry
+      const int blk = meta_blk(lo);
+      for (int n = 0; n < 16; ++n) m0s[n] = meta_scale(n, blk);
+      for (int n = 0; n < 16; ++n) m0z[n] = meta_zero(n, blk);
+      iss(s0, lo);
+      mid();
+      for (int n = 0; n < 16; ++n) *mp_at(0, n, ment) = meta_pack(m0s[n], m0z[n], blk, p.has_z);
+    } else {
+      iss(s0, lo);
+      mid();
+    }
+    loop(iss);
+  };
   if (wave < W / 2) {
-    auto consume0 = [&](RowStage<MT, NS>& s, int b) { consume(s, b, [] {}); };
-    pipeline2(lo, hi, NS, s0, s1, issue, consume0);
+    run(std::integral_constant<int, 0>{}, [&](auto& iss) {
+      auto consume0 = [&](RowStage<MT, NS>& s, int b) {
+        consume(s, b, [] {}, std::integral_constant<int, 0>{});
+      };
+      pipeline2(lo, hi, NS, s0, s1, iss, consume0);
+    });
   } else {
-    pipeline2_late(lo, hi, NS, s0, s1, issue, consume);
+    run(std::integral_constant<int, 1>{}, [&](auto& iss) {
+      auto consume1 = [&](RowStage<MT, NS>& s, int b, auto&& after) {
+        consume(s, b, after, std::integral_constant<int, 1>{});
+      };
+      pipeline2_late(lo, hi, NS, s0, s1, iss, consume1);
+    });
   }
 
   if constexpr (!GROUPED) {  // per-channel: one scale per row
