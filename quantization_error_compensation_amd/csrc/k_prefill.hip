@@ -203,8 +203,10 @@ __global__ __launch_bounds__(512, 1) void prefill_kernel(PrefillParams p) {
   // loads of blocks kb and kb + 1 are in flight (7 each with group scales,
   // 6 without, after any chunk loads issued ahead of them); waiting until at
   // most that many remain completes block kb (and the chunk loads of kb + 1),
-  // and the barrier makes every wave's part of it visible.  Past the barrier every wave has finished reading block
-  // kb - 1, so its stage takes the loads of block kb + 2.  Past the last
+  // and the barrier makes every wave's part of it visible.  Past the barrier
+  // every wave has finished reading block kb - 1, so its stage takes the
+  // loads of block kb + 2 (issued by each wave once per iteration, before or
+  // after its compute, see below).  Past the last
   // block the loads repeat block kb1 - 1 into the free stage, which keeps the
   // count of loads in flight the same in every iteration.
   //
@@ -231,7 +233,14 @@ __global__ __launch_bounds__(512, 1) void prefill_kernel(PrefillParams p) {
     __builtin_amdgcn_s_waitcnt(0xC07F);
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
-    issue(min(kb + 2, kb1 - 1), (i + 2) % kStages, kb + 2 < kb1 && ((kb + 2) & 7) == 0);
+    // Loads of block kb + 2: the second half of the waves issues them here,
+    // the first half after this block's compute (below).  The two waves of
+    // a SIMD compute a block at the same time and the first half gets the
+    // SIMD first; its loads, issued when its compute is done, wait at the
+    // memory pipeline while the second half still computes, and the second
+    // half's own loads meet a shorter queue here.
+    if (wave >= kPrefillWaves / 2)
+      issue(min(kb + 2, kb1 - 1), (i + 2) % kStages, kb + 2 < kb1 && ((kb + 2) & 7) == 0);
 
     const uint8_t* X = smem + (i % kStages) * kStage;
     const uint8_t* W = X + kXStage;
@@ -298,6 +307,8 @@ __global__ __launch_bounds__(512, 1) void prefill_kernel(PrefillParams p) {
     wc[1] = wd[1][1][3];
     scc[0] = sc[0];
     scc[1] = sc[1];
+    if (wave < kPrefillWaves / 2)
+      issue(min(kb + 2, kb1 - 1), (i + 2) % kStages, kb + 2 < kb1 && ((kb + 2) & 7) == 0);
   }
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   // The last block's last step and fold.
