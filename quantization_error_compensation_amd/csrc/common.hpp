@@ -1,16 +1,18 @@
 // Device helpers shared by the libspear_ec kernels (gfx950 / CDNA4).
 //
 // Integer-code operands.  The matrix cores take bf16 operands.  An int4 code c
-// is turned into the bf16 value 128 + c with one bit operation: 0x4300 is
-// 128.0 in bf16 and the low 7 mantissa bits then count units, so OR-ing a
-// nibble into them gives 128 + c exactly.  Eight codes of a 32-bit word become
-// four packed bf16 pairs with four AND-OR operations and three shifts.  The
-// products (128 + c) * x are exact in fp32; the offset is removed with the
-// per-block sums of x:
+// is turned into the bf16 value 128 + c by placing its nibble under the
+// exponent byte: 0x4300 is 128.0 in bf16 and the low 7 mantissa bits then
+// count units.  Eight codes of a 32-bit word become four packed bf16 pairs
+// with two masks, one shift and four byte permutes.  The products
+// (128 + c) * x are exact in fp32, and the offset comes out in the matrix
+// cores as well:
 //     sum_k (c_k - z) x_k = sum_k (128 + c_k) x_k - (128 + z) * sum_k x_k,
-// and the group scale s is applied in fp32.  Nothing is rounded to bf16 on
-// the weight side, so the dequantized weight the layer sees is the exact
-// (c - z) * s of the format.
+// -(128 + z) being exact in bf16 (decode multiplies x by it in every K step;
+// prefill multiplies it by the block sums of x, split into three bf16
+// parts, in one extra K step per block).  The group scale s is applied in
+// fp32.  Nothing is rounded to bf16 on the weight side, so the dequantized
+// weight the layer sees is the exact (c - z) * s of the format.
 //
 // K order.  The pairs built from a word hold columns (0,2), (4,6), (1,3),
 // (5,7) of its eight, so a matrix-core operand carries the columns of an

@@ -35,8 +35,9 @@
 //     read 16 different rows slowed the address unit), turned into the
 //     matrix-core layout (lane = row) through a wave-private LDS area when
 //     the burst computes; bf16 operands 128 + c by byte permutes;
-//   * group scale and zero-point word of the lane's row: one small load each
-//     per block, straight into registers;
+//   * group scales and zero-points: staged per wave in LDS by chunks of 16
+//     bursts (one packed word per row and block), one row of the next chunk
+//     loaded with each burst;
 //   * matrix cores 16x16x32: tokens (padded to 16 or 32) x 16 rows x 32 K;
 //     each K step also multiplies x by the exact bf16 -(128 + z), which
 //     removes the codes' offset inside the same fp32 chain (block sums of x
@@ -382,7 +383,7 @@ __device__ void rank_segment(const DecodeParams& p, int rb, int lo, int hi, uint
 // own LDS area by chunks of C blocks counted from the segment start
 // (chunk j: blocks lo + C j .., C = 16 NS), two chunks at a time: slot j % 2
 // holds one 32-bit word per (row, block), the scale's fp16 bits in the low
-// half and -(128 + z) as fp16 (exact) in the high half, rows C + 4 words
+// half and the bf16 bits of -(128 + z) (exact) in the high half, rows C + 4 words
 // apart (a burst's NS words are one 8- or 16-byte read).  The first chunk is
 // loaded with the segment's first burst; then each burst of chunk j loads
 // one row of chunk j + 1 (a scale and its zero-point word per lane), packed
@@ -425,9 +426,9 @@ struct RowStage {
 };
 
 // Rows BR band + 16 wave + c16 (this wave's tile), blocks [lo, hi): partial
-// y with the scales applied.  Per block and token the result is
-// s (P - (128 + z) S), P the matrix-core product with the 128 + c operands
-// and S the block sum of x.
+// y with the scales applied.  Per block and token the result is s P, P the
+// matrix-core chain over the block's K steps of x times the 128 + c
+// operands and of x times -(128 + z), that is the sum of (c - z) x.
 
 // mid() runs while the segment's first loads are in flight (scalar work
 // that the segment does not need).
