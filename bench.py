@@ -71,12 +71,39 @@ def layer_flops(K, N, r, T, serq=False):
     return 2 * T * K * N + 2 * T * r * (K + N) + 4 * T * r
 
 
+def _code_only(src):
+    """C++ source with its comments removed and blank runs collapsed, so that
+    a change to comments alone leaves the hash (and the measurements tied to
+    it) in place."""
+    out, i, n = [], 0, len(src)
+    while i < n:
+        c = src[i]
+        if c in "\"'":  # string or character literal, copied whole
+            j = i + 1
+            while j < n and src[j] != c:
+                j += 2 if src[j] == "\\" else 1
+            out.append(src[i:j + 1])
+            i = j + 1
+        elif src.startswith("//", i):
+            while i < n and src[i] != "\n":
+                i += 1
+        elif src.startswith("/*", i):
+            j = src.find("*/", i + 2)
+            i = n if j < 0 else j + 2
+            out.append(" ")
+        else:
+            out.append(c)
+            i += 1
+    return " ".join("".join(out).split())
+
+
 def kernel_source_hash():
+    """Hash of the kernel sources' code (comments and layout excluded)."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "quantization_error_compensation_amd", "csrc")
     for f in sorted(os.listdir(csrc)):
-        with open(os.path.join(csrc, f), "rb") as fh:
-            h.update(f.encode() + fh.read())
+        with open(os.path.join(csrc, f), encoding="utf-8") as fh:
+            h.update(f.encode() + _code_only(fh.read()).encode())
     return h.hexdigest()[:16]
 
 
