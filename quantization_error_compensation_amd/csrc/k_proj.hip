@@ -42,7 +42,7 @@ struct ProjParams {
   float* wv32;         // [T][r]
   uint16_t* wvhi;      // [T][r]
   uint16_t* wvlo;      // [T][r]
-  int T, K, r, Tp, splits;
+  int T, K, r, Tp, splits, tiles;
 };
 
 // The x tile (kProjTokens tokens) and all r rows of A for one 128-column
@@ -66,7 +66,14 @@ __global__ __launch_bounds__(256, 1) void projection_kernel(ProjParams p) {
 
   const int lane = threadIdx.x & 63, wave = wave_id();
   const int q = lane >> 4, c16 = lane & 15;
-  const int tile = blockIdx.x, split = blockIdx.y;
+  // Workgroup -> (tile, split), split-major: the tiles of one K split are
+  // adjacent, and runs of adjacent workgroups are placed on one XCD
+  // (workgroups are dealt to the 8 XCDs round-robin), so each XCD fetches
+  // only its splits' columns of A into its L2 instead of all of A.
+  const int total = p.tiles * p.splits;
+  int idx = blockIdx.x;
+  if ((total & 7) == 0) idx = (blockIdx.x & 7) * (total >> 3) + (blockIdx.x >> 3);
+  const int split = idx / p.tiles, tile = idx - split * p.tiles;
   const int KB = p.K / kBlockK;
   const int kb0 = (int)((long long)KB * split / p.splits);
   const int kb1 = (int)((long long)KB * (split + 1) / p.splits);
@@ -266,7 +273,8 @@ hipError_t launch_projection(const Shape& s, const LayerArgs& a, const WsPtrs& w
   p.r = s.r;
   p.Tp = pl.tiles * kProjTokens;
   p.splits = pl.splits;
-  const dim3 grid(pl.tiles, pl.splits);
+  p.tiles = pl.tiles;
+  const dim3 grid(pl.tiles * pl.splits);
   hipError_t e;
   switch (s.r / 16) {
     case 0: e = launch_rtx<0>(p, grid, st); break;
