@@ -22,7 +22,10 @@
 // partial sums), the rank workgroups take no rows at all ("separate" mode,
 // S = Rw, D = 0) and the rows are split over the other P - Rw.  On the cost
 // axis each row band boundary takes X units (row_cost), so a run that
-// crosses one carries fewer units.  Row parts
+// crosses one carries fewer units.  Where the runs are short (under 32
+// units) and the row workgroups take no rank units, the planner launches
+// S + M NB workgroups instead, M per row band, with X = 0: every M-th run
+// then starts a band and none crosses one.  Row parts
 // start on an even block of their band, so the bursts' code loads stay on
 // 128-byte lines; every workgroup from S on keeps at least one row unit.
 //
