@@ -33,9 +33,13 @@ DecodePlan plan_decode(const Shape& s, int slots) {
   pl.bands = (s.N + kDecodeBandRows - 1) / kDecodeBandRows;
   pl.rank_bands = s.serq ? 0 : (s.r + 63) / 64;  // SERQ takes x's channels, no projection
   slots = std::min(std::max(slots, 1), kMaxSlots);
-  pl.split = make_split(KB, pl.rank_bands, pl.bands, slots);
+  // Rank workgroups also stream rows ("shared" mode) only with group-wise
+  // scales, where the device tests run that mode (one and two rank bands);
+  // per-channel layers keep them apart ("separate" mode).
+  const bool shared = s.grouped;
+  pl.split = make_split(KB, pl.rank_bands, pl.bands, slots, shared);
   pl.workgroups = pl.split.P;
-  pl.slots = split_workspace_slots(KB, pl.rank_bands, pl.bands, kMaxSlots);
+  pl.slots = split_workspace_slots(KB, pl.rank_bands, pl.bands, kMaxSlots, shared);
   return pl;
 }
 

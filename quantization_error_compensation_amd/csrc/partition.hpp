@@ -20,7 +20,10 @@
 // first go on to stream rows).  When the rank units would take more than
 // half of a workgroup's share (short row runs would cut bands into many
 // partial sums), the rank workgroups take no rows at all ("separate" mode,
-// S = Rw, D = 0) and the rows are split over the other P - Rw.  On the cost
+// S = Rw, D = 0) and the rows are split over the other P - Rw; the caller
+// can ask for separate mode outright (the library does for layers with
+// per-channel scales, whose shared-mode splits no device test covers).  On
+// the cost
 // axis each row band boundary takes X units (row_cost), so a run that
 // crosses one carries fewer units.  Where the runs are short (under 32
 // units) and the row workgroups take no rank units, the planner launches
@@ -208,8 +211,9 @@ constexpr int kBoundaryShare = 4;
 constexpr int kAlignedShare = 32;
 
 // The split for P_max = slots workgroups, before the band boundaries are
-// given a cost.  Host only.
-inline DecodeSplit make_split_flat(int KB, int RB, int NB, int slots) {
+// given a cost.  shared = false keeps the rank workgroups off the rows
+// (separate mode) whatever the sizes.  Host only.
+inline DecodeSplit make_split_flat(int KB, int RB, int NB, int slots, bool shared = true) {
   DecodeSplit d;
   d.X = 0;
   d.KB = KB;
@@ -240,7 +244,7 @@ inline DecodeSplit make_split_flat(int KB, int RB, int NB, int slots) {
   const long long rw_sh = (RU + kRankUnitsPerWg - 1) / kRankUnitsPerWg < slots
                               ? (RU + kRankUnitsPerWg - 1) / kRankUnitsPerWg
                               : slots;
-  if (p_sh >= rw_sh && p_sh >= 2 && (Rw < 1 || p_sh >= p_sep)) {
+  if (shared && p_sh >= rw_sh && p_sh >= 2 && (Rw < 1 || p_sh >= p_sep)) {
     d.S = 1;
     d.P = (int)p_sh;
     d.D = (int)D;
@@ -263,8 +267,8 @@ inline DecodeSplit make_split_flat(int KB, int RB, int NB, int slots) {
 }
 
 // The split with the band boundaries' cost.  Host only.
-inline DecodeSplit make_split_plain(int KB, int RB, int NB, int slots) {
-  DecodeSplit d = make_split_flat(KB, RB, NB, slots);
+inline DecodeSplit make_split_plain(int KB, int RB, int NB, int slots, bool shared = true) {
+  DecodeSplit d = make_split_flat(KB, RB, NB, slots, shared);
   const int Pp = d.P - d.S;
   const long long share = Pp > 0 ? (long long)d.C / Pp : 0;
   // Short runs, and no rank work on the row workgroups: M row workgroups
@@ -290,15 +294,15 @@ inline DecodeSplit make_split_plain(int KB, int RB, int NB, int slots) {
   return d;
 }
 
-inline DecodeSplit make_split(int KB, int RB, int NB, int slots) {
-  return with_divisors(make_split_plain(KB, RB, NB, slots));
+inline DecodeSplit make_split(int KB, int RB, int NB, int slots, bool shared = true) {
+  return with_divisors(make_split_plain(KB, RB, NB, slots, shared));
 }
 
 // Partial-sum slots a workspace holds for a layer: enough for the split at
 // any slot count up to max_slots (P and Rw only shrink with fewer slots): two
 // per workgroup of the largest split, two per rank workgroup at most.  Host.
-inline int split_workspace_slots(int KB, int RB, int NB, int max_slots) {
-  const DecodeSplit big = make_split(KB, RB, NB, max_slots);
+inline int split_workspace_slots(int KB, int RB, int NB, int max_slots, bool shared = true) {
+  const DecodeSplit big = make_split(KB, RB, NB, max_slots, shared);
   const long long RU = (long long)RB * KB;
   long long rw = (RU + kRankUnitsPerWg - 1) / kRankUnitsPerWg;
   if (rw > max_slots) rw = max_slots;

@@ -49,16 +49,18 @@ extern "C" int check_fastdiv(uint32_t dmax) {
 // 0 = all checks hold; otherwise g_msg says which failed.  stats (may be
 // NULL): P, Rw, S, D, max segments of a row band, max segments of a rank
 // band, workspace slots, max row units of one workgroup.
-extern "C" int check_split(int KB, int RB, int NB, int slots, int max_slots, long long* stats) {
+extern "C" int check_split(int KB, int RB, int NB, int slots, int max_slots, int shared,
+                           long long* stats) {
   g_msg[0] = 0;
-  const DecodeSplit d = make_split(KB, RB, NB, slots);
-  const int ws_slots = split_workspace_slots(KB, RB, NB, max_slots);
+  const DecodeSplit d = make_split(KB, RB, NB, slots, shared != 0);
+  const int ws_slots = split_workspace_slots(KB, RB, NB, max_slots, shared != 0);
   const long long RU = split_ru(d), WU = split_wu(d);
   REQUIRE(d.KB == KB && d.RB == RB && d.NB == NB, "split fields");
   REQUIRE(d.P >= 1 && d.P <= (slots < 1 ? 1 : slots), "P=%d outside [1, %d]", d.P, slots);
   // rank work: workgroup 0 reduces it and takes no rows, unless it is alone
   REQUIRE(RB == 0 ? d.S == 0 : (d.P == 1 ? d.S == 0 : (d.S == 1 || d.S == d.Rw)),
           "S=%d Rw=%d P=%d", d.S, d.Rw, d.P);
+  REQUIRE(shared || RB == 0 || d.P == 1 || d.S == d.Rw, "shared mode when asked for separate");
   REQUIRE(RB == 0 ? d.Rw == 0 : (d.Rw >= 1 && d.Rw <= d.P && d.Rw <= RU), "Rw=%d", d.Rw);
   REQUIRE(d.S < d.P, "no workgroup takes rows (S=%d P=%d)", d.S, d.P);
 

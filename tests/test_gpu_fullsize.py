@@ -20,6 +20,8 @@ the workspace error word zero.
 """
 from __future__ import annotations
 
+import dataclasses
+
 import concurrent.futures as cf
 
 import numpy as np
@@ -135,7 +137,10 @@ class FullLayer:
         spec = self.spec
         alpha = spec.alpha if alpha is None else alpha
         x = synth.activations(spec, T)
-        A, B, gv, bv = synth.compensator(spec, r)
+        # a rank above the layer's own is drawn from a spec of that rank
+        cspec = spec if r <= spec.rank else dataclasses.replace(spec, rank=r)
+        A, B, gv, bv = synth.compensator(cspec, r)
+        assert A.shape == (r, self.K) and B.shape == (self.N, r), (A.shape, B.shape)
         desc = q.make_desc(self.K, self.N, r, self.g, self.asym, spec.per_tensor, out_f32=f32)
         y = torch.empty((T, self.N), dtype=torch.float32 if f32 else torch.bfloat16, device="cuda")
         ws = q.alloc_workspace(desc, T)
@@ -153,7 +158,7 @@ class FullLayer:
 @pytest.mark.parametrize("name,runs", [
     ("c1", [(1, 32), (8, 32), (32, 32)]),
     ("c2", [(2048, 64), (1, 64)]),
-    ("c3", [(16, 64), (512, 64), (1, 64), (32, 64)]),
+    ("c3", [(16, 64), (512, 64), (1, 64), (32, 64), (16, 128)]),  # r 128: two rank bands
     ("c4", [(T, r) for T in (1, 16, 256, 4096) for r in synth.C4_RANKS]),
     ("v1", [(9, 0), (2, 0), (5, 0)]),
 ])

@@ -30,7 +30,7 @@ def lib():
     subprocess.check_call(["g++", "-std=c++17", "-O2", "-shared", "-fPIC", "-D__HIP_PLATFORM_AMD__",
                            *extra, "-I/opt/rocm/include", "-I", CSRC, SRC, "-o", out])
     L = ctypes.CDLL(out)
-    L.check_split.argtypes = [ctypes.c_int] * 5 + [ctypes.POINTER(ctypes.c_longlong)]
+    L.check_split.argtypes = [ctypes.c_int] * 6 + [ctypes.POINTER(ctypes.c_longlong)]
     L.check_split.restype = ctypes.c_int
     L.check_message.restype = ctypes.c_char_p
     L.check_fastdiv.argtypes = [ctypes.c_uint32]
@@ -43,11 +43,11 @@ def test_fast_division_matches_the_divider(lib):
     assert lib.check_fastdiv(1100) == 0, lib.check_message().decode()
 
 
-def run(lib, K, N, r, slots):
+def run(lib, K, N, r, slots, shared=True):
     KB, NB, RB = K // 128, (N + 127) // 128, (r + 63) // 64
     st = (ctypes.c_longlong * 8)()
-    rc = lib.check_split(KB, RB, NB, slots, MAX_SLOTS, st)
-    assert rc == 0, (K, N, r, slots, lib.check_message().decode())
+    rc = lib.check_split(KB, RB, NB, slots, MAX_SLOTS, int(shared), st)
+    assert rc == 0, (K, N, r, slots, shared, lib.check_message().decode())
     return dict(zip(("P", "Rw", "S", "D", "seg_row", "seg_rank", "ws_slots", "maxrun"), list(st)))
 
 
@@ -60,6 +60,15 @@ LAYERS = [(128, 16), (128, 128), (256, 16), (512, 512), (1024, 48), (4096, 4096)
 def test_split_holds_for_every_slot_count(lib, K, N, r):
     for slots in (1, 2, 3, 7, 32, 100, 255, 256):
         run(lib, K, N, r, slots)
+        run(lib, K, N, r, slots, shared=False)
+
+
+def test_separate_mode_when_asked(lib):
+    # the 70B layer at rank 128 (two rank bands) would share its rank
+    # workgroups with rows; asked for separate mode it keeps them apart
+    assert run(lib, 28672, 8192, 128, 256)["S"] == 1
+    st = run(lib, 28672, 8192, 128, 256, shared=False)
+    assert st["S"] == st["Rw"] > 1, st
 
 
 def test_large_layers(lib):
