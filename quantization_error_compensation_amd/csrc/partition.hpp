@@ -23,14 +23,13 @@
 // S = Rw, D = 0) and the rows are split over the other P - Rw; the caller
 // can ask for separate mode outright (the library does for layers with
 // per-channel scales, whose shared-mode splits no device test covers).  On
-// the cost
-// axis each row band boundary takes X units (row_cost), so a run that
-// crosses one carries fewer units.  Where the runs are short (under 32
+// the cost axis each row band boundary takes X units (row_cost), so a run
+// that crosses one carries fewer units.  Where the runs are short (under 32
 // units) and the row workgroups take no rank units, the planner launches
 // S + M NB workgroups instead, M per row band, with X = 0: every M-th run
-// then starts a band and none crosses one.  Row parts
-// start on an even block of their band, so the bursts' code loads stay on
-// 128-byte lines; every workgroup from S on keeps at least one row unit.
+// then starts a band and none crosses one.  Row parts start on an even
+// block of their band, so the bursts' code loads stay on 128-byte lines;
+// every workgroup from S on keeps at least one row unit.
 //
 // Arithmetic.  Unit counts stay below 2^21 (KB, NB <= 1024, RB <= 2) and the
 // cost axis below 2^22, so every numerator here (at most P <= 256 times a
